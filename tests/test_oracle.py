@@ -1,0 +1,383 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+* a worked example with exact rational answers (tests/golden/hand_worked_small.json);
+* a scalar brute force with math.fsum on tiny shapes;
+* a library special case (torch float64 softmax / logsumexp on CPU);
+* closed forms: Q = 0 gives the mean of the visible V rows and LSE = ln |J(i)|;
+  a single key gives V[0] and LSE = scale·q·k0; constant V columns come back;
+* invariants: rows of P sum to 1, key shift (with scores far beyond exp's range),
+  key permutation, split + reduction = unsplit, two identical splits add ln 2.
+
+A mutation test plants plausible mistakes in the oracle (on the CPU) and checks
+that at least one pin catches each of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import exact as oa
+from oracle.brute import attention_brute
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_small.json")
+
+
+def _val(x):
+    if isinstance(x, (int, float)):
+        return float(x)
+    x = x.strip()
+    if x.startswith("ln "):
+        return math.log(float(Fraction(x[3:])))
+    if x == "ln(2)":
+        return math.log(2.0)
+    return float(Fraction(x))
+
+
+def _arr(nested):
+    if isinstance(nested, list):
+        return np.array([_arr(e) for e in nested])
+    return _val(nested)
+
+
+def _rand(b, s_q, s_k, h, d, seed):
+    r = np.random.default_rng(seed)
+    return r.standard_normal((b, s_q, h, d)), r.standard_normal((b, s_k, h, d)), \
+        r.standard_normal((b, s_k, h, d))
+
+
+# ---------------------------------------------------------------- pins ----
+# Each pin raises AssertionError (or any error) when the oracle is wrong.
+
+def pin_golden():
+    g = json.load(open(GOLDEN))
+    q, k, v = _arr(g["q"]), _arr(g["k"]), _arr(g["v"])
+    scale = _val(g["scale"])
+    for mode, causal in (("noncausal", False), ("causal", True)):
+        O, L = oracle.attention(q, k, v, scale, causal)
+        np.testing.assert_allclose(O, _arr(g["expected"][mode]["O"]), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(L, _arr(g["expected"][mode]["LSE"]), rtol=0, atol=1e-13)
+    sp = g["expected"]["split_row0"]
+    bounds = [tuple(b) for b in sp["bounds"]]
+    Op, Lp = oracle.attention_split(q, k, v, scale, False, bounds)
+    np.testing.assert_allclose(Op[:, 0, 0, 0, :], _arr(sp["O_parts"]), atol=1e-13)
+    np.testing.assert_allclose(Lp[:, 0, 0, 0], _arr(sp["LSE_parts"]), atol=1e-13)
+    O, L = oracle.combine(Op, Lp)
+    np.testing.assert_allclose(O[0, 0, 0], _arr(sp["O"]), atol=1e-13)
+    np.testing.assert_allclose(L[0, 0, 0], _val(sp["LSE"]), atol=1e-13)
+
+
+BRUTE_SHAPES = [
+    # b, s_q, s_k, h, d
+    (1, 1, 1, 1, 1),
+    (2, 3, 5, 2, 4),
+    (1, 7, 4, 2, 8),   # s_q > s_k: causal rows 0..2 see nothing
+    (2, 9, 9, 1, 3),
+    (1, 5, 8, 2, 2),
+]
+
+
+def pin_brute():
+    for n, (b, s_q, s_k, h, d) in enumerate(BRUTE_SHAPES):
+        q, k, v = _rand(b, s_q, s_k, h, d, 100 + n)
+        scale = 0.7
+        for causal in (False, True):
+            O, L = oracle.attention(q, k, v, scale, causal)
+            Ob, Lb = attention_brute(q, k, v, scale, causal)
+            np.testing.assert_allclose(O, np.array(Ob), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(L, np.array(Lb), rtol=0, atol=1e-12)
+
+
+def pin_torch_special_case():
+    # Library routine: torch CPU float64 softmax and logsumexp of the masked score
+    # matrix, built in the (b, h, s, d) layout of the tutorial's standard attention.
+    b, s_q, s_k, h, d = 2, 6, 10, 3, 8
+    q, k, v = _rand(b, s_q, s_k, h, d, 7)
+    scale = 1 / math.sqrt(d)
+    for causal in (False, True):
+        tq, tk, tv = (torch.from_numpy(x).transpose(1, 2) for x in (q, k, v))
+        S = torch.matmul(tq, tk.transpose(-1, -2)) * scale
+        if causal:
+            i = torch.arange(s_q)[:, None]
+            j = torch.arange(s_k)[None, :]
+            S = S.masked_fill(j > i + (s_k - s_q), float("-inf"))
+        P = torch.softmax(S, dim=-1)
+        O_ref = torch.matmul(P, tv).transpose(1, 2).numpy()
+        L_ref = torch.logsumexp(S, dim=-1).numpy()
+        O, L = oracle.attention(q, k, v, scale, causal)
+        np.testing.assert_allclose(O, O_ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L, L_ref, rtol=0, atol=1e-12)
+
+
+def pin_rows_sum_to_one():
+    r = np.random.default_rng(3)
+    S = r.standard_normal((4, 5, 9)) * 30
+    S[0, 1, 3:] = -np.inf
+    S[2, 4, :] = -np.inf  # empty row
+    P, m, lse = oracle.softmax_rows(S)
+    sums = P.sum(-1)
+    want = np.ones_like(sums)
+    want[2, 4] = 0.0
+    np.testing.assert_allclose(sums, want, atol=1e-12)
+    assert np.all(P[0, 1, 3:] == 0) and np.all(P >= 0)
+    assert lse[2, 4] == -np.inf and m[2, 4] == -np.inf
+    np.testing.assert_allclose(lse[1, 2], np.log(np.exp(S[1, 2]).sum()), rtol=1e-13)
+
+
+def pin_constant_v():
+    b, s_q, s_k, h, d = 2, 7, 11, 2, 4
+    q, k, v = _rand(b, s_q, s_k, h, d, 11)
+    v[:, :, :, 1] = 0.75
+    v[:, :, 1, 3] = -2.5
+    for causal in (False, True):
+        O, _ = oracle.attention(q, k, v, 0.9, causal)
+        np.testing.assert_allclose(O[:, :, :, 1], 0.75, rtol=1e-14)
+        np.testing.assert_allclose(O[:, :, 1, 3], -2.5, rtol=1e-14)
+
+
+def pin_q_zero_closed_form():
+    for (s_q, s_k) in ((6, 6), (4, 9), (8, 5)):
+        b, h, d = 2, 2, 4
+        _, k, v = _rand(b, s_q, s_k, h, d, 5)
+        q = np.zeros((b, s_q, h, d))
+        for causal in (False, True):
+            O, L = oracle.attention(q, k, v, 0.5, causal)
+            for i in range(s_q):
+                cnt = s_k if not causal else max(0, min(s_k, i + s_k - s_q + 1))
+                if cnt == 0:
+                    assert np.all(O[:, i] == 0) and np.all(L[:, :, i] == -np.inf)
+                    continue
+                np.testing.assert_allclose(O[:, i], v[:, :cnt].mean(axis=1), atol=1e-13)
+                np.testing.assert_allclose(L[:, :, i], math.log(cnt), atol=1e-13)
+
+
+def pin_single_key():
+    b, s_q, h, d = 2, 3, 2, 5
+    q, k, v = _rand(b, s_q, 1, h, d, 9)
+    O, L = oracle.attention(q, k, v, 0.3, False)
+    np.testing.assert_allclose(O, np.broadcast_to(v, O.shape), atol=1e-15)
+    dots = np.einsum("bshd,bhd->bhs", q, k[:, 0])
+    np.testing.assert_allclose(L, 0.3 * dots, atol=1e-13)
+    # causal with s_q == s_k: row 0 sees key 0 only
+    q2, k2, v2 = _rand(1, 4, 4, 1, 3, 21)
+    O2, L2 = oracle.attention(q2, k2, v2, 0.3, True)
+    np.testing.assert_allclose(O2[0, 0, 0], v2[0, 0, 0], atol=1e-15)
+    np.testing.assert_allclose(L2[0, 0, 0], 0.3 * q2[0, 0, 0] @ k2[0, 0, 0], atol=1e-14)
+    Onc, Lnc = oracle.attention(q2, k2, v2, 0.3, False)
+    np.testing.assert_allclose(O2[0, 3], Onc[0, 3], atol=1e-15)
+
+
+def pin_key_shift():
+    # Scores reach ~±2000: exp without the max subtracted overflows float64.
+    b, s_q, s_k, h, d = 1, 5, 12, 2, 4
+    q, k, v = _rand(b, s_q, s_k, h, d, 13)
+    u = np.array([300.0, -200.0, 150.0, 250.0])
+    k2 = k + u
+    for causal in (False, True):
+        O, L = oracle.attention(q, k, v, 1.0, causal)
+        O2, L2 = oracle.attention(q, k2, v, 1.0, causal)
+        np.testing.assert_allclose(O2, O, atol=1e-10)
+        np.testing.assert_allclose(L2, L + np.einsum("bshd,d->bhs", q, u), rtol=1e-12)
+        assert np.all(np.isfinite(O2))
+
+
+def pin_key_permutation():
+    b, s_q, s_k, h, d = 2, 4, 9, 2, 3
+    q, k, v = _rand(b, s_q, s_k, h, d, 17)
+    perm = np.random.default_rng(1).permutation(s_k)
+    O, L = oracle.attention(q, k, v, 0.8, False)
+    O2, L2 = oracle.attention(q, k[:, perm], v[:, perm], 0.8, False)
+    np.testing.assert_allclose(O2, O, atol=1e-13)
+    np.testing.assert_allclose(L2, L, atol=1e-13)
+
+
+def pin_split_equals_unsplit():
+    b, s_q, s_k, h, d = 2, 6, 13, 2, 4
+    q, k, v = _rand(b, s_q, s_k, h, d, 19)
+    q[0, 0, 0] *= 200  # a row with a large score range
+    for causal in (False, True):
+        O, L = oracle.attention(q, k, v, 0.6, causal)
+        for n in (1, 2, 3, 7, s_k):
+            Op, Lp = oracle.attention_split(q, k, v, 0.6, causal, oracle.split_bounds(s_k, n))
+            O2, L2 = oracle.combine(Op, Lp)
+            np.testing.assert_allclose(O2, O.transpose(0, 2, 1, 3), atol=1e-12)
+            np.testing.assert_allclose(L2, L, atol=1e-12)
+        # uneven, hand-chosen bounds including an empty range
+        bounds = [(0, 1), (1, 1), (1, 8), (8, 13)]
+        Op, Lp = oracle.attention_split(q, k, v, 0.6, causal, bounds)
+        assert np.all(Lp[1] == -np.inf) and np.all(Op[1] == 0)
+        O2, L2 = oracle.combine(Op, Lp)
+        np.testing.assert_allclose(O2, O.transpose(0, 2, 1, 3), atol=1e-12)
+        np.testing.assert_allclose(L2, L, atol=1e-12)
+
+
+def pin_identical_splits():
+    r = np.random.default_rng(23)
+    o = r.standard_normal((2, 3, 4))
+    lse = r.standard_normal((2, 3)) * 50
+    O, L = oracle.combine(np.stack([o, o]), np.stack([lse, lse]))
+    np.testing.assert_allclose(O, o, atol=1e-13)
+    np.testing.assert_allclose(L, lse + math.log(2), atol=1e-12)
+    # all splits empty: O = 0, LSE = -inf
+    O, L = oracle.combine(np.zeros((3, 2, 4)), np.full((3, 2), -np.inf))
+    assert np.all(O == 0) and np.all(L == -np.inf)
+
+
+def pin_rows_subset():
+    b, s_q, s_k, h, d = 1, 20, 20, 2, 4
+    q, k, v = _rand(b, s_q, s_k, h, d, 29)
+    rows = [[0, 3, 19], [1, 2, 18]]
+    for causal in (False, True):
+        O, L = oracle.attention(q, k, v, 0.4, causal)
+        Or, Lr = oracle.attention_rows(q, k, v, 0.4, causal, rows)
+        for hi in range(h):
+            np.testing.assert_allclose(Or[:, hi], O[:, rows[hi], hi], atol=1e-14)
+            np.testing.assert_allclose(Lr[:, hi], L[:, hi, rows[hi]], atol=1e-14)
+
+
+PINS = [pin_golden, pin_brute, pin_torch_special_case, pin_rows_sum_to_one, pin_constant_v,
+        pin_q_zero_closed_form, pin_single_key, pin_key_shift, pin_key_permutation,
+        pin_split_equals_unsplit, pin_identical_splits, pin_rows_subset]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+# ------------------------------------------------------------ mutants ----
+# Each mutant replaces one oracle helper with a plausible wrong version.
+
+_REAL_SOFTMAX = oa.softmax_rows
+_REAL_ATTEND = oa._attend
+_REAL_COMBINE = oa.combine
+
+def _softmax_no_max(S):
+    E = np.exp(S)
+    l = E.sum(-1)
+    with np.errstate(all="ignore"):
+        return E / l[..., None], S.max(-1), np.log(l)
+
+
+def _softmax_lse_without_max(S):
+    P, m, lse = _REAL_SOFTMAX(S)
+    return P, m, np.where(np.isfinite(m), lse - m, lse)
+
+
+def _mask_top_left(s_q, s_k, causal, rows=None):
+    rows = np.arange(s_q) if rows is None else np.asarray(rows)
+    if not causal:
+        return np.ones((rows.size, s_k), dtype=bool)
+    return np.arange(s_k)[None, :] <= rows[:, None]
+
+
+def _mask_off_by_one(s_q, s_k, causal, rows=None):
+    rows = np.arange(s_q) if rows is None else np.asarray(rows)
+    if not causal:
+        return np.ones((rows.size, s_k), dtype=bool)
+    return np.arange(s_k)[None, :] < rows[:, None] + (s_k - s_q)
+
+
+def _attend_no_scale(qh, kh, vh, scale, mask):
+    return _REAL_ATTEND(qh, kh, vh, 1.0, mask)
+
+
+def _attend_sqrt_scale(qh, kh, vh, scale, mask):
+    return _REAL_ATTEND(qh, kh, vh, math.sqrt(abs(scale)), mask)
+
+
+def _attend_pv_with_k(qh, kh, vh, scale, mask):
+    return _REAL_ATTEND(qh, kh, kh if kh.shape == vh.shape else vh, scale, mask)
+
+
+def _attend_transposed_p(qh, kh, vh, scale, mask):
+    S = scale * np.matmul(qh, np.swapaxes(kh, -1, -2))
+    S = np.where(mask, S, -np.inf)
+    P, _, lse = oa.softmax_rows(S)
+    if P.shape[-1] == P.shape[-2]:
+        P = np.swapaxes(P, -1, -2)
+    return np.matmul(P, vh), lse
+
+
+def _combine_no_max(o_parts, lse_parts):
+    with np.errstate(all="ignore"):
+        w = np.exp(lse_parts)
+        lse = np.log(w.sum(0))
+        return (np.exp(lse_parts - lse[None])[..., None] * o_parts).sum(0), lse
+
+
+def _combine_unweighted(o_parts, lse_parts):
+    O, lse = _REAL_COMBINE(o_parts, lse_parts)
+    return o_parts.mean(0), lse
+
+
+MUTANTS = {
+    "softmax_no_max": ("softmax_rows", _softmax_no_max),
+    "lse_without_max": ("softmax_rows", _softmax_lse_without_max),
+    "causal_top_left": ("visible_mask", _mask_top_left),
+    "causal_off_by_one": ("visible_mask", _mask_off_by_one),
+    "no_scale": ("_attend", _attend_no_scale),
+    "sqrt_scale": ("_attend", _attend_sqrt_scale),
+    "pv_uses_k": ("_attend", _attend_pv_with_k),
+    "p_transposed": ("_attend", _attend_transposed_p),
+    "combine_no_max": ("combine", _combine_no_max),
+    "combine_unweighted": ("combine", _combine_unweighted),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(oa, attr, fn)
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, fn)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin in PINS:
+            try:
+                pin()
+            except Exception:
+                caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
+
+
+# ------------------------------------------------------ input recipe ----
+
+def test_inputs_are_seeded_and_rounded():
+    q1, k1, v1 = workloads.make_qkv(2, 5, 7, 3, 16, "bf16", seed=42)
+    q2, k2, v2 = workloads.make_qkv(2, 5, 7, 3, 16, "bf16", seed=42)
+    assert q1.dtype == torch.bfloat16 and k1.shape == (2, 7, 3, 16)
+    assert torch.equal(q1, q2) and torch.equal(k1, k2) and torch.equal(v1, v2)
+    q3, _, _ = workloads.make_qkv(2, 5, 7, 3, 16, "bf16", seed=43)
+    assert not torch.equal(q1, q3)
+    # q, k, v come from one generator in that order: k is not a copy of q's stream start
+    assert not torch.equal(q1.flatten()[:16], k1.flatten()[:16])
+    qh, _, _ = workloads.make_qkv(1, 64, 64, 2, 32, "fp16")
+    x = qh.float()
+    assert abs(x.mean().item()) < 0.1 and abs(x.std().item() - 1) < 0.1
+
+
+def test_sample_rows():
+    rows = workloads.sample_rows(16384, 256, 4, seed=42)
+    assert len(rows) == 4 and all(len(r) == 256 for r in rows)
+    for r in rows:
+        assert r == sorted(set(r)) and r[0] == 0 and r[-1] == 16383
+        assert {0, 1, 63, 64, 127, 128, 255, 256} <= set(r)
+    assert rows[0] != rows[1]
+    assert rows == workloads.sample_rows(16384, 256, 4, seed=42)
+    small = workloads.sample_rows(50, 256, 2)
+    assert small[0] == list(range(50))
+
+
+def test_workload_table():
+    W = workloads.WORKLOADS
+    assert [W[c].d for c in ("C1", "C2", "C3", "C4", "C5")] == [16, 16, 128, 128, 128]
+    assert W["C5"].causal and not W["C3"].causal
+    assert W["C4"].s_q == 1 and W["C4"].s_k == 32768 and W["C4"].kind == "decode"
+    assert W["C2"].b == 512 and W["C2"].s_q == 150
+    assert abs(W["C3"].scale - 1 / math.sqrt(128)) < 1e-15
