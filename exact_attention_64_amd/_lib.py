@@ -1,0 +1,217 @@
+"""ctypes binding of ``libattn.so`` (the gfx950 C ABI declared in include/attn.h).
+
+Argument marshalling only: torch tensors are turned into device pointers,
+element strides and the current HIP stream, outputs are allocated with torch
+when the caller does not pass them, and every status code is turned into an
+exception.  All attention arithmetic runs in the HIP kernels; if the library is
+not built this module raises instead of computing anything itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+ATTN_FP16, ATTN_BF16 = 0, 1
+ATTN_MAX_SPLITS = 256
+_DTYPE_CODE = {torch.float16: ATTN_FP16, torch.bfloat16: ATTN_BF16}
+_CODE_DTYPE = {v: k for k, v in _DTYPE_CODE.items()}
+
+STATUS = {0: "ATTN_OK", -1: "ATTN_E_NULL", -2: "ATTN_E_DTYPE", -3: "ATTN_E_SHAPE",
+          -4: "ATTN_E_HEADDIM", -5: "ATTN_E_LAYOUT", -6: "ATTN_E_SCALE", -7: "ATTN_E_SPLITS",
+          -8: "ATTN_E_DEVICE", -9: "ATTN_E_LAUNCH"}
+
+I64x3 = ctypes.c_int64 * 3
+
+# Every symbol include/attn.h declares.
+EXPORTS = ("attn_fwd", "attn_num_splits", "attn_num_splits_for", "attn_fwd_splitkv",
+           "attn_combine", "attn_status_str")
+
+
+class AttnArgs(ctypes.Structure):
+    """Mirror of ``attn_args``."""
+
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("b", ctypes.c_int64), ("s_q", ctypes.c_int64), ("s_k", ctypes.c_int64),
+        ("h", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("q_stride", I64x3), ("k_stride", I64x3), ("v_stride", I64x3), ("o_stride", I64x3),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"{STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """Load ``libattn.so`` once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build the HIP library first "
+                    "(python -m exact_attention_64_amd.build)")
+            L = ctypes.CDLL(LIB_PATH)
+            P = ctypes.POINTER
+            L.attn_fwd.argtypes = [P(AttnArgs), ctypes.c_void_p]
+            L.attn_fwd.restype = ctypes.c_int32
+            L.attn_num_splits.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int, P(ctypes.c_int32)]
+            L.attn_num_splits.restype = ctypes.c_int32
+            L.attn_num_splits_for.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int32, P(ctypes.c_int32)]
+            L.attn_num_splits_for.restype = ctypes.c_int32
+            L.attn_fwd_splitkv.argtypes = [P(AttnArgs), ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+            L.attn_fwd_splitkv.restype = ctypes.c_int32
+            L.attn_combine.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                       ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_void_p,
+                                       ctypes.c_void_p]
+            L.attn_combine.restype = ctypes.c_int32
+            L.attn_status_str.argtypes = [ctypes.c_int32]
+            L.attn_status_str.restype = ctypes.c_char_p
+            _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise AttnError(status, lib().attn_status_str(status).decode())
+
+
+def status_str(status: int) -> str:
+    return lib().attn_status_str(status).decode()
+
+
+def _stream_ptr(t: torch.Tensor, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _bshd(name, t: torch.Tensor):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D (b, s, h, d), got shape {tuple(t.shape)}")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name} must have a contiguous last (head-dim) dimension")
+    return I64x3(t.stride(0), t.stride(1), t.stride(2))
+
+
+def make_args(q, k, v, softmax_scale=None, causal=False, out=None, lse=None) -> AttnArgs:
+    """Fill ``attn_args`` from (b, s, h, d) tensors (no copies)."""
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share dtype float16 or bfloat16")
+    b, s_q, h, d = q.shape
+    s_k = k.shape[1]
+    if tuple(k.shape) != (b, s_k, h, d) or tuple(v.shape) != (b, s_k, h, d):
+        raise ValueError(f"k and v must be (b, s_k, h, d) = ({b}, s_k, {h}, {d})")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    a = AttnArgs()
+    a.dtype = _DTYPE_CODE[q.dtype]
+    a.causal = 1 if causal else 0
+    a.b, a.s_q, a.s_k, a.h, a.d = b, s_q, s_k, h, d
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.q_stride, a.k_stride, a.v_stride = _bshd("q", q), _bshd("k", k), _bshd("v", v)
+    if out is not None:
+        if tuple(out.shape) != (b, s_q, h, d) or out.dtype != q.dtype:
+            raise ValueError("out must match q's shape and dtype")
+        a.o = out.data_ptr()
+        a.o_stride = _bshd("out", out)
+    if lse is not None:
+        if tuple(lse.shape) != (b, h, s_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 (b, h, s_q) tensor")
+        a.lse = lse.data_ptr()
+    a.softmax_scale = float(softmax_scale)
+    return a
+
+
+def attn_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, stream=None,
+             return_lse=True):
+    """Fused exact attention forward. Returns (O, LSE) (LSE None if not requested)."""
+    b, s_q, h, d = q.shape
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None and return_lse:
+        lse = torch.empty((b, h, s_q), dtype=torch.float32, device=q.device)
+    a = make_args(q, k, v, softmax_scale, causal, out, lse)
+    _check(lib().attn_fwd(ctypes.byref(a), _stream_ptr(q, stream)))
+    return out, lse
+
+
+def attn_num_splits(b, h, s_q, s_k, d, device=None) -> int:
+    n = ctypes.c_int32(0)
+    dev = torch.cuda.current_device() if device is None else int(device)
+    _check(lib().attn_num_splits(b, h, s_q, s_k, d, dev, ctypes.byref(n)))
+    return n.value
+
+
+def attn_num_splits_for(b, h, s_q, s_k, d, num_cus) -> int:
+    n = ctypes.c_int32(0)
+    _check(lib().attn_num_splits_for(b, h, s_q, s_k, d, num_cus, ctypes.byref(n)))
+    return n.value
+
+
+def attn_fwd_splitkv(q, k, v, num_splits=0, softmax_scale=None, causal=False, o_part=None,
+                     lse_part=None, stream=None):
+    """First flash-decoding stage. Returns fp32 (O_parts [n,b,h,s_q,d], LSE_parts [n,b,h,s_q])."""
+    b, s_q, h, d = q.shape
+    s_k = k.shape[1]
+    if num_splits == 0:
+        num_splits = attn_num_splits(b, h, s_q, s_k, d, q.device.index)
+    if o_part is None:
+        o_part = torch.empty((num_splits, b, h, s_q, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((num_splits, b, h, s_q), dtype=torch.float32, device=q.device)
+    if (tuple(o_part.shape) != (num_splits, b, h, s_q, d) or not o_part.is_contiguous()
+            or tuple(lse_part.shape) != (num_splits, b, h, s_q) or not lse_part.is_contiguous()
+            or o_part.dtype != torch.float32 or lse_part.dtype != torch.float32):
+        raise ValueError("o_part / lse_part must be dense fp32 [n,b,h,s_q,d] / [n,b,h,s_q]")
+    a = make_args(q, k, v, softmax_scale, causal)
+    _check(lib().attn_fwd_splitkv(ctypes.byref(a), num_splits, ctypes.c_void_p(o_part.data_ptr()),
+                                  ctypes.c_void_p(lse_part.data_ptr()), _stream_ptr(q, stream)))
+    return o_part, lse_part
+
+
+def attn_combine(o_part, lse_part, dtype=torch.bfloat16, out=None, lse=None, stream=None,
+                 return_lse=True):
+    """Second flash-decoding stage. Returns (O (b,s_q,h,d) dtype, LSE (b,h,s_q) fp32)."""
+    n, b, h, s_q, d = o_part.shape
+    if tuple(lse_part.shape) != (n, b, h, s_q) or not (o_part.is_contiguous() and lse_part.is_contiguous()):
+        raise ValueError("o_part / lse_part must be dense [n,b,h,s_q,d] / [n,b,h,s_q]")
+    if out is None:
+        out = torch.empty((b, s_q, h, d), dtype=dtype, device=o_part.device)
+    if lse is None and return_lse:
+        lse = torch.empty((b, h, s_q), dtype=torch.float32, device=o_part.device)
+    if out.dtype not in _DTYPE_CODE:
+        raise TypeError("out must be float16 or bfloat16")
+    ostr = _bshd("out", out)
+    _check(lib().attn_combine(n, b, h, s_q, d, ctypes.c_void_p(o_part.data_ptr()),
+                              ctypes.c_void_p(lse_part.data_ptr()), _DTYPE_CODE[out.dtype],
+                              ctypes.c_void_p(out.data_ptr()), ostr,
+                              ctypes.c_void_p(lse.data_ptr() if lse is not None else None),
+                              _stream_ptr(o_part, stream)))
+    return out, lse
+
+
+def attn_decode(q, k, v, num_splits=0, softmax_scale=None, causal=False, stream=None):
+    """Split-KV forward followed by the combine: flash-decoding end to end."""
+    o_part, lse_part = attn_fwd_splitkv(q, k, v, num_splits, softmax_scale, causal, stream=stream)
+    return attn_combine(o_part, lse_part, q.dtype, stream=stream)

@@ -1,0 +1,72 @@
+"""Build the gfx950 HIP library ``libattn.so`` in-tree with hipcc.
+
+Usage: ``python -m exact_attention_64_amd.build`` (or ``build()`` from Python).
+Always recompiles; the result lands next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libattn.so")
+
+SOURCES = ["attn_api.cpp", "attn_kernels.hip"]
+
+# Packed fp32 VALU instructions are switched off for every HIP translation unit.
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wno-unused-command-line-argument"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP library cannot be built")
+
+
+def build(verbose: bool = False, jobs: int = 2) -> str:
+    """Compile every source for gfx950 and link ``libattn.so``. Returns its path."""
+    cc = hipcc()
+    objs = []
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(HERE, "_build", src + ".o")
+        os.makedirs(os.path.dirname(obj), exist_ok=True)
+        cmd = [cc, *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
+        if src.endswith(".cpp"):
+            cmd.insert(1, "-x")
+            cmd.insert(2, "hip")
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        objs.append(obj)
+    failed = []
+    for src, pr in procs:
+        out, _ = pr.communicate()
+        text = out.decode(errors="replace")
+        keep = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+        if pr.returncode != 0:
+            failed.append((src, "\n".join(keep)))
+        elif verbose and keep:
+            print("\n".join(keep))
+    if failed:
+        msg = "\n\n".join(f"--- {s}\n{t}" for s, t in failed)
+        raise RuntimeError(f"hipcc failed:\n{msg}")
+    tmp = LIB + ".tmp"
+    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,239 @@
+// C-ABI front end: argument validation, the split-count heuristic, per-device
+// capability cache and kernel dispatch.  Every check runs on the host before
+// any launch; on error nothing is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool strides_ok(const int64_t s[3]) {
+  for (int i = 0; i < 3; ++i)
+    if (s[i] < 0 || (s[i] % 8) != 0) return false;
+  return true;
+}
+
+bool headdim_ok(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+attn_status check_shape(int64_t b, int64_t h, int64_t s_q, int64_t s_k) {
+  if (b < 1 || h < 1 || s_q < 1 || s_k < 1) return ATTN_E_SHAPE;
+  if (s_q > ATTN_MAX_SEQ || s_k > ATTN_MAX_SEQ) return ATTN_E_SHAPE;
+  if (b > ATTN_MAX_BH || h > ATTN_MAX_BH || b * h > ATTN_MAX_BH) return ATTN_E_SHAPE;
+  return ATTN_OK;
+}
+
+// Common checks of attn_args.  need_o: O and its strides are used.
+attn_status check_args(const attn_args* a, bool need_o) {
+  if (!a) return ATTN_E_NULL;
+  if (!a->q || !a->k || !a->v || (need_o && !a->o)) return ATTN_E_NULL;
+  if (a->dtype != ATTN_FP16 && a->dtype != ATTN_BF16) return ATTN_E_DTYPE;
+  attn_status st = check_shape(a->b, a->h, a->s_q, a->s_k);
+  if (st != ATTN_OK) return st;
+  if (!headdim_ok(a->d)) return ATTN_E_HEADDIM;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v)) return ATTN_E_LAYOUT;
+  if (!strides_ok(a->q_stride) || !strides_ok(a->k_stride) || !strides_ok(a->v_stride)) return ATTN_E_LAYOUT;
+  if (need_o && (!aligned16(a->o) || !strides_ok(a->o_stride))) return ATTN_E_LAYOUT;
+  if (need_o && a->lse && !aligned4(a->lse)) return ATTN_E_LAYOUT;
+  if (!std::isfinite(a->softmax_scale)) return ATTN_E_SCALE;
+  return ATTN_OK;
+}
+
+struct DevInfo {
+  bool filled = false;
+  bool gfx950 = false;
+  int cus = 0;
+};
+std::mutex g_mu;
+DevInfo g_dev[64];
+
+attn_status device_info(int dev, DevInfo* out) {
+  if (dev < 0 || dev >= 64) return ATTN_E_DEVICE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  DevInfo& d = g_dev[dev];
+  if (!d.filled) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_E_DEVICE;
+    d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    d.filled = true;
+  }
+  *out = d;
+  return ATTN_OK;
+}
+
+attn_status current_device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return ATTN_E_DEVICE;
+  }
+  DevInfo info;
+  attn_status st = device_info(dev, &info);
+  if (st != ATTN_OK) return st;
+  return info.gfx950 ? ATTN_OK : ATTN_E_DEVICE;
+}
+
+void fill_params(const attn_args* a, attn::FwdParams* p) {
+  std::memset(p, 0, sizeof(*p));
+  p->q = a->q;
+  p->k = a->k;
+  p->v = a->v;
+  p->o = a->o;
+  p->lse = a->lse;
+  for (int i = 0; i < 3; ++i) {
+    p->qs[i] = a->q_stride[i];
+    p->ks[i] = a->k_stride[i];
+    p->vs[i] = a->v_stride[i];
+    p->os[i] = a->o_stride[i];
+  }
+  p->b = (int)a->b;
+  p->h = (int)a->h;
+  p->s_q = (int)a->s_q;
+  p->s_k = (int)a->s_k;
+  p->d = (int)a->d;
+  p->n_splits = 1;
+  const float s = a->softmax_scale;
+  // The kernels work in base 2 with log2(e) folded into the scale.  A negative
+  // scale is applied by negating Q on load; a zero scale by zeroing Q (then every
+  // score is exactly 0, as the definition requires).
+  p->zero_q = s == 0.f;
+  p->neg_q = s < 0.f;
+  p->scale_log2 = s == 0.f ? 1.f : std::fabs(s) * 1.4426950408889634f;
+}
+
+bool grid_ok(const attn_args* a, int64_t n_splits) {
+  const int64_t bm = attn::fwd_rows_per_block((int)a->d);
+  const int64_t grid = ceil_div(a->s_q, bm) * a->b * a->h * n_splits;
+  return grid <= 0x7fffffff;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(int32_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_NULL: return "a required pointer is NULL";
+    case ATTN_E_DTYPE: return "dtype must be ATTN_FP16 or ATTN_BF16";
+    case ATTN_E_SHAPE: return "b, h, s_q and s_k must be >= 1 and within the size limits";
+    case ATTN_E_HEADDIM: return "head dim must be 16, 32, 64 or 128";
+    case ATTN_E_LAYOUT: return "pointers must be 16-byte aligned and strides non-negative multiples of 8 elements";
+    case ATTN_E_SCALE: return "softmax_scale must be finite";
+    case ATTN_E_SPLITS: return "num_splits must be in [1, min(s_k, ATTN_MAX_SPLITS)]";
+    case ATTN_E_DEVICE: return "no usable gfx950 device";
+    case ATTN_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+attn_status attn_fwd(const attn_args* a, void* stream) {
+  attn_status st = check_args(a, true);
+  if (st != ATTN_OK) return st;
+  if (!grid_ok(a, 1)) return ATTN_E_SHAPE;
+  st = current_device_ok();
+  if (st != ATTN_OK) return st;
+  attn::FwdParams p;
+  fill_params(a, &p);
+  hipError_t e = attn::launch_fwd(p, a->dtype, a->causal != 0, false, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+attn_status attn_num_splits_for(int64_t b, int64_t h, int64_t s_q, int64_t s_k, int64_t d,
+                                int32_t num_cus, int32_t* n_out) {
+  if (!n_out) return ATTN_E_NULL;
+  attn_status st = check_shape(b, h, s_q, s_k);
+  if (st != ATTN_OK) return st;
+  if (!headdim_ok(d)) return ATTN_E_HEADDIM;
+  if (num_cus < 1) return ATTN_E_DEVICE;
+  // Parallel work without splitting: one work-group per (b, h, query row block).
+  const int64_t work = b * h * ceil_div(s_q, attn::fwd_rows_per_block((int)d));
+  int64_t n = 1;
+  if (work < num_cus) {
+    // About two work-groups per compute unit, each split keeping >= 64 keys.
+    n = ceil_div(2 * (int64_t)num_cus, work);
+    n = n < ceil_div(s_k, 64) ? n : ceil_div(s_k, 64);
+    n = n < ATTN_MAX_SPLITS ? n : ATTN_MAX_SPLITS;
+    n = n < 1 ? 1 : n;
+  }
+  *n_out = (int32_t)n;
+  return ATTN_OK;
+}
+
+attn_status attn_num_splits(int64_t b, int64_t h, int64_t s_q, int64_t s_k, int64_t d, int device,
+                            int32_t* n_out) {
+  if (!n_out) return ATTN_E_NULL;
+  attn_status st = check_shape(b, h, s_q, s_k);
+  if (st != ATTN_OK) return st;
+  if (!headdim_ok(d)) return ATTN_E_HEADDIM;
+  DevInfo info;
+  st = device_info(device, &info);
+  if (st != ATTN_OK) return st;
+  if (!info.gfx950) return ATTN_E_DEVICE;
+  return attn_num_splits_for(b, h, s_q, s_k, d, info.cus, n_out);
+}
+
+attn_status attn_fwd_splitkv(const attn_args* a, int32_t num_splits, float* o_part, float* lse_part,
+                             void* stream) {
+  attn_status st = check_args(a, false);
+  if (st == ATTN_OK && (!o_part || !lse_part)) st = ATTN_E_NULL;
+  if (st != ATTN_OK) return st;
+  if (!aligned16(o_part) || !aligned4(lse_part)) return ATTN_E_LAYOUT;
+  const int64_t max_n = a->s_k < ATTN_MAX_SPLITS ? a->s_k : ATTN_MAX_SPLITS;
+  if (num_splits < 1 || num_splits > max_n) return ATTN_E_SPLITS;
+  if (!grid_ok(a, num_splits)) return ATTN_E_SHAPE;
+  st = current_device_ok();
+  if (st != ATTN_OK) return st;
+  attn::FwdParams p;
+  fill_params(a, &p);
+  p.o = nullptr;
+  p.lse = nullptr;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.n_splits = num_splits;
+  hipError_t e = attn::launch_fwd(p, a->dtype, a->causal != 0, true, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+attn_status attn_combine(int32_t num_splits, int64_t b, int64_t h, int64_t s_q, int64_t d,
+                         const float* o_part, const float* lse_part, int32_t dtype, void* o,
+                         const int64_t o_stride[3], float* lse, void* stream) {
+  if (!o_part || !lse_part || !o || !o_stride) return ATTN_E_NULL;
+  if (dtype != ATTN_FP16 && dtype != ATTN_BF16) return ATTN_E_DTYPE;
+  attn_status st = check_shape(b, h, s_q, 1);
+  if (st != ATTN_OK) return st;
+  if (b * h * s_q > 0x7fffffff) return ATTN_E_SHAPE;
+  if (!headdim_ok(d)) return ATTN_E_HEADDIM;
+  if (!aligned16(o_part) || !aligned4(lse_part) || !aligned16(o) || !strides_ok(o_stride) ||
+      (lse && !aligned4(lse)))
+    return ATTN_E_LAYOUT;
+  if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return ATTN_E_SPLITS;
+  st = current_device_ok();
+  if (st != ATTN_OK) return st;
+  attn::CombineParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.o = o;
+  p.lse = lse;
+  for (int i = 0; i < 3; ++i) p.os[i] = o_stride[i];
+  p.b = (int)b;
+  p.h = (int)h;
+  p.s_q = (int)s_q;
+  p.d = (int)d;
+  p.n_splits = num_splits;
+  hipError_t e = attn::launch_combine(p, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,505 @@
+// Exact attention forward kernels for gfx950 (MI355X).
+//
+// The fused kernel follows "LLM Lab Notes 07: Why FlashAttention Is Fast":
+// the score matrix is produced one tile at a time and never stored (section 3.1,
+// tiling), K/V tiles pass through on-chip LDS and only O and LSE are written back
+// (section 3.2, IO-awareness), and the running row maximum rescales the partial
+// output whenever it grows, which keeps the result exact (section 3.3, online
+// softmax).  The split-KV variant and the combine kernel implement the two stages
+// of flash-decoding discussed in flash-attention issue #1248 ("where is flash
+// decoding second stage (reduce) code?").
+//
+// Data flow of the fused kernel (one work-group = NW waves, 64*RB... rows each):
+//   Q fragment   : registers, loaded once, in the B-operand layout of
+//                  v_mfma_f32_32x32x16_{bf16,f16}.
+//   K, V tiles   : BN keys x D, global -> registers -> LDS, double-buffered.
+//   S^T = K Q^T  : MFMA, so each lane owns one query row and 16 of every 32 keys
+//                  and the row maximum needs one permlane32 swap.
+//   P            : exp2 of the scaled scores minus the running maximum (log2(e)
+//                  folded into the scale), rounded to the input type.
+//   O^T += V^T P^T : MFMA; V^T fragments come from ds_read_b64_tr_b16.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_internal.h"
+
+namespace attn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From& x) {
+  static_assert(sizeof(To) == sizeof(From), "size");
+  return __builtin_bit_cast(To, x);
+}
+
+// Per-dtype pieces: the MFMA flavour and float -> storage rounding (nearest even).
+template <int DT> struct Ty;
+template <> struct Ty<kBF16> {
+  static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack2(float x, float y) {
+    bf16x2_t v = {(__bf16)x, (__bf16)y};
+    return bitcast<unsigned>(v);
+  }
+  static __device__ __forceinline__ unsigned short one(float x) { return bitcast<unsigned short>((__bf16)x); }
+};
+template <> struct Ty<kFP16> {
+  static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<f16x8_t>(a), bitcast<f16x8_t>(b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack2(float x, float y) {
+    f16x2_t v = {(_Float16)x, (_Float16)y};
+    return bitcast<unsigned>(v);
+  }
+  static __device__ __forceinline__ unsigned short one(float x) { return bitcast<unsigned short>((_Float16)x); }
+};
+
+// Maximum of a value and its partner lane (lane ^ 32), in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------
+// LDS tile layouts.  A tile holds BN rows (keys) of D elements; a row is NCH
+// 16-byte chunks.  Chunks are XOR-swizzled per row so that the two read
+// patterns below touch all 64 LDS banks without conflicts:
+//  K: ds_read_b128, 16 consecutive lanes read one chunk column of 16 rows;
+//  V: ds_read_b64_tr_b16, a half-wave reads 64 bytes of each of 4 rows.
+template <int D> struct Swz {
+  static constexpr int NCH = D / 8;
+  static __device__ __forceinline__ int k(int row) {
+    return (row / (16 / NCH)) % NCH;
+  }
+  static __device__ __forceinline__ int v(int row) {
+    return NCH == 16 ? 4 * (row % 4) : (NCH == 8 ? 4 * ((row / 2) % 2) : 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Fused forward kernel.
+//   T_ : kBF16 / kFP16.  D: head dim.  NW: waves per work-group.
+//   RB : 32-row blocks per wave.  BN: keys per tile.  SPLIT: write fp32
+//   per-split partials (flash-decoding first stage) instead of O / LSE.
+template <int T_, int D, int NW, int RB, int BN, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(const FwdParams p) {
+  using Tt = Ty<T_>;
+  constexpr int NCH = D / 8;               // 16-byte chunks per row
+  constexpr int KK = D / 16;               // k-steps of the S^T MFMA
+  constexpr int NB = BN / 32;              // 32-key blocks per tile
+  constexpr int CB = D >= 32 ? D / 32 : 1; // 32-row (d) blocks of O^T
+  constexpr int BM = NW * RB * 32;         // query rows per work-group
+  constexpr int NT = NW * 64;
+  constexpr int TILE_BYTES = BN * D * 2;
+  constexpr int CPT = (BN * NCH + NT - 1) / NT;  // staged chunks per thread per tensor
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;  // which half of the wave
+
+  // ---- work-group -> (q tile, batch*head, split); heaviest causal tiles first
+  const int per_qt = p.b * p.h * p.n_splits;
+  const int qt_rev = blockIdx.x / per_qt;
+  const int rem = blockIdx.x - qt_rev * per_qt;
+  const int bh = rem / p.n_splits;
+  const int split = rem - bh * p.n_splits;
+  const int qt = CAUSAL ? (p.n_qt - 1 - qt_rev) : qt_rev;
+  const int bb = bh / p.h;
+  const int hh = bh - bb * p.h;
+  const int q0 = qt * BM;
+  const int off = p.s_k - p.s_q;  // bottom-right causal offset
+
+  int k_lo = 0, k_hi = p.s_k;
+  if (SPLIT) {
+    k_lo = (int)(((int64_t)split * p.s_k) / p.n_splits);
+    k_hi = (int)(((int64_t)(split + 1) * p.s_k) / p.n_splits);
+  }
+  if (CAUSAL) k_hi = min(k_hi, q0 + BM + off);
+  const int ntiles = k_hi > k_lo ? (k_hi - k_lo + BN - 1) / BN : 0;
+
+  const unsigned short* __restrict__ Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
+  const unsigned short* __restrict__ Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hh * p.ks[2];
+  const unsigned short* __restrict__ Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hh * p.vs[2];
+
+  const int qw0 = q0 + wave * RB * 32;  // first query row of this wave
+
+  // ---- Q fragments (B operand of S^T = K Q^T): row qw0 + rb*32 + l32, d = hi*8 + 16*kk
+  u32x4_t qf[RB][KK];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int i = qw0 + rb * 32 + l32;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (i < p.s_q && !p.zero_q) {
+        x = *(const u32x4_t*)(Qg + (int64_t)i * p.qs[1] + hi * 8 + kk * 16);
+        if (p.neg_q) x ^= 0x80008000u;
+      }
+      qf[rb][kk] = x;
+    }
+  }
+
+  f32x16_t o[CB][RB];
+  float m[RB], l[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[cb][rb][r] = 0.f;
+  }
+  const float c = p.scale_log2;
+
+  // ---- staging: chunk f of a tile -> row f / NCH, chunk f % NCH
+  u32x4_t stk[CPT], stv[CPT];
+  auto stage_load = [&](int t) {
+    const int k0 = k_lo + t * BN;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int f = tid + i * NT;
+      u32x4_t xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+      if (f < BN * NCH) {
+        const int row = f / NCH, ch = f % NCH;
+        const int key = k0 + row;
+        if (key < k_hi) {
+          xk = *(const u32x4_t*)(Kg + (int64_t)key * p.ks[1] + ch * 8);
+          xv = *(const u32x4_t*)(Vg + (int64_t)key * p.vs[1] + ch * 8);
+        }
+      }
+      stk[i] = xk;
+      stv[i] = xv;
+    }
+  };
+  auto stage_store = [&](int buf) {
+    char* kb = smem + buf * 2 * TILE_BYTES;
+    char* vb = kb + TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int f = tid + i * NT;
+      if (f < BN * NCH) {
+        const int row = f / NCH, ch = f % NCH;
+        *(u32x4_t*)(kb + row * D * 2 + 16 * (ch ^ Swz<D>::k(row))) = stk[i];
+        *(u32x4_t*)(vb + row * D * 2 + 16 * (ch ^ Swz<D>::v(row))) = stv[i];
+      }
+    }
+  };
+
+  const bool wave_live = qw0 < p.s_q;
+  const int wave_last_key = qw0 + RB * 32 - 1 + off;  // causal visibility of the wave's last row
+
+  if (ntiles > 0) {
+    stage_load(0);
+    stage_store(0);
+    __syncthreads();
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) stage_load(t + 1);
+    const int k0 = k_lo + t * BN;
+    const bool skip = !wave_live || (CAUSAL && k0 > wave_last_key);
+    if (!skip) {
+      const char* kb = smem + (t & 1) * 2 * TILE_BYTES;
+      const char* vb = kb + TILE_BYTES;
+      // S^T = K Q^T
+      f32x16_t s[NB][RB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[nb][rb][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int row = nb * 32 + l32;
+          const int ch = hi + 2 * kk;
+          const u32x4_t kf = *(const u32x4_t*)(kb + row * D * 2 + 16 * (ch ^ Swz<D>::k(row)));
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) s[nb][rb] = Tt::mfma(kf, qf[rb][kk], s[nb][rb]);
+        }
+      }
+      // masks: keys past the range end, and (causal) keys after the diagonal
+      const bool need_mask = (k0 + BN > k_hi) || (CAUSAL && k0 + BN - 1 > qw0 + off);
+      if (need_mask) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int i = qw0 + rb * 32 + l32;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = k0 + nb * 32 + (r / 4) * 8 + hi * 4 + (r % 4);
+              const bool bad = key >= k_hi || (CAUSAL && key > i + off);
+              if (bad) s[nb][rb][r] = -INFINITY;
+            }
+        }
+      }
+      // online softmax, base 2, log2(e) folded into c
+      u32x4_t pf[RB][BN / 16];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][rb][r]);
+        mx = pair_max(mx);
+        const float m_new = fmaxf(m[rb], mx * c);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m[rb] - m_use);
+        float lsum = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][rb][r], c, -m_use));
+            s[nb][rb][r] = pv;
+            lsum += pv;
+          }
+        l[rb] = l[rb] * alpha + lsum;
+        m[rb] = m_new;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[cb][rb][r] *= alpha;
+#pragma unroll
+        for (int t16 = 0; t16 < BN / 16; ++t16) {
+          u32x4_t x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x[e] = Tt::pack2(s[t16 / 2][rb][8 * (t16 % 2) + 2 * e], s[t16 / 2][rb][8 * (t16 % 2) + 2 * e + 1]);
+          pf[rb][t16] = x;
+        }
+      }
+      // O^T += V^T P^T.  A-operand lane layout: d row cb*32 + l32, keys
+      // 16*t16 + 4*hi + {0..3} and 16*t16 + 8 + 4*hi + {0..3}; each half comes
+      // from one transposed LDS read in which lane x of a 16-lane group fetches
+      // 4 columns of key row (x / 4).
+      const int g16 = (lane >> 4) & 1;      // column half within the 32-wide block
+      const int xr = (lane & 15) >> 2;      // key row within the group of 4
+      const int xq = lane & 3;              // 4-column quad
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        int col = cb * 32 + g16 * 16 + xq * 4;
+        if (D < 32) col &= (D - 1);         // D=16: the upper 16 rows of O^T are unused
+        const int ch = col / 8, half = (col % 8) / 4;
+#pragma unroll
+        for (int t16 = 0; t16 < BN / 16; ++t16) {
+          u32x4_t vf;
+#pragma unroll
+          for (int rd = 0; rd < 2; ++rd) {
+            const int row = 16 * t16 + 8 * rd + 4 * hi + xr;
+            const char* a = vb + row * D * 2 + 16 * (ch ^ Swz<D>::v(row)) + 8 * half;
+            const s16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(a));
+            const u32x2_t yy = bitcast<u32x2_t>(y);
+            vf[2 * rd] = yy[0];
+            vf[2 * rd + 1] = yy[1];
+          }
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) o[cb][rb] = Tt::mfma(vf, pf[rb][t16], o[cb][rb]);
+        }
+      }
+    }
+    if (t + 1 < ntiles) stage_store((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int i = qw0 + rb * 32 + l32;
+    const float lt = pair_sum(l[rb]);
+    const bool has = lt > 0.f;
+    const float inv = has ? 1.f / lt : 0.f;
+    const float lse = has ? (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    if (i < p.s_q) {
+      if (SPLIT) {
+        const int64_t rowi = (((int64_t)split * p.b + bb) * p.h + hh) * p.s_q + i;
+        float* op = p.o_part + rowi * D;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int col = cb * 32 + r4 * 8 + hi * 4;
+            if (col < D) {
+              f32x4_t x = {o[cb][rb][4 * r4] * inv, o[cb][rb][4 * r4 + 1] * inv,
+                           o[cb][rb][4 * r4 + 2] * inv, o[cb][rb][4 * r4 + 3] * inv};
+              *(f32x4_t*)(op + col) = x;
+            }
+          }
+        if (hi == 0) p.lse_part[rowi] = lse;
+      } else {
+        unsigned short* op = (unsigned short*)p.o + (int64_t)bb * p.os[0] + (int64_t)i * p.os[1] + (int64_t)hh * p.os[2];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int col = cb * 32 + r4 * 8 + hi * 4;
+            if (col < D) {
+              u32x2_t x = {Tt::pack2(o[cb][rb][4 * r4] * inv, o[cb][rb][4 * r4 + 1] * inv),
+                           Tt::pack2(o[cb][rb][4 * r4 + 2] * inv, o[cb][rb][4 * r4 + 3] * inv)};
+              *(u32x2_t*)(op + col) = x;
+            }
+          }
+        if (hi == 0 && p.lse) p.lse[((int64_t)bb * p.h + hh) * p.s_q + i] = lse;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split reduction (issue #1248): one work-group per (b, h, row).
+//   LSE = M + ln sum_i exp(LSE_i - M),  M = max_i LSE_i
+//   O   = sum_i exp(LSE_i - LSE) * O_i
+// Splits are summed in increasing order inside each of G lane groups, then the
+// G group sums in increasing group order, so the result is deterministic.
+template <int T_, int D>
+__global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
+  using Tt = Ty<T_>;
+  constexpr int TPS = D / 4;         // threads per split row (float4 each)
+  constexpr int G = 256 / TPS;       // split rows in flight
+  __shared__ float w_s[kMaxSplits];
+  __shared__ float red[256];
+  __shared__ f32x4_t acc_s[G][TPS];
+
+  const int row = blockIdx.x;  // (b*h + head)*s_q + i
+  const int tid = threadIdx.x;
+  const int n = p.n_splits;
+  const int64_t rows = (int64_t)p.b * p.h * p.s_q;
+
+  float mloc = -INFINITY;
+  for (int i = tid; i < n; i += 256) {
+    const float x = p.lse_part[(int64_t)i * rows + row];
+    w_s[i] = x;
+    mloc = fmaxf(mloc, x);
+  }
+  red[tid] = mloc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  const float Ms = M == -INFINITY ? 0.f : M;
+  float sloc = 0.f;
+  for (int i = tid; i < n; i += 256) sloc += __expf(w_s[i] - Ms);
+  red[tid] = sloc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  const float tot = red[0];
+  const bool has = M != -INFINITY && tot > 0.f;
+  const float lse = has ? Ms + __logf(tot) : -INFINITY;
+  __syncthreads();
+  for (int i = tid; i < n; i += 256) w_s[i] = has ? __expf(w_s[i] - lse) : 0.f;
+  __syncthreads();
+
+  const int g = tid / TPS, c4 = tid % TPS;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i = g; i < n; i += G) {
+    const float w = w_s[i];
+    const f32x4_t x = *(const f32x4_t*)(p.o_part + ((int64_t)i * rows + row) * D + c4 * 4);
+    acc += w * x;
+  }
+  acc_s[g][c4] = acc;
+  __syncthreads();
+  if (tid < TPS) {
+    f32x4_t a = acc_s[0][tid];
+    for (int gg = 1; gg < G; ++gg) a += acc_s[gg][tid];
+    const int i = row % p.s_q;
+    const int bh = row / p.s_q;
+    const int bb = bh / p.h, hh = bh % p.h;
+    unsigned short* op = (unsigned short*)p.o + (int64_t)bb * p.os[0] + (int64_t)i * p.os[1] + (int64_t)hh * p.os[2];
+    u32x2_t x = {Tt::pack2(a[0], a[1]), Tt::pack2(a[2], a[3])};
+    *(u32x2_t*)(op + tid * 4) = x;
+    if (tid == 0 && p.lse) p.lse[row] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+
+template <int T_, int D, int NW, int RB, int BN, bool CAUSAL, bool SPLIT>
+static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t st) {
+  constexpr int BM = NW * RB * 32;
+  FwdParams q = p;
+  q.n_qt = (p.s_q + BM - 1) / BM;
+  const int64_t grid = (int64_t)q.n_qt * p.b * p.h * p.n_splits;
+  hipLaunchKernelGGL((fwd_kernel<T_, D, NW, RB, BN, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
+  return hipGetLastError();
+}
+
+template <int T_, int D, bool CAUSAL, bool SPLIT>
+static hipError_t launch_fwd_d(const FwdParams& p, hipStream_t st) {
+  if constexpr (D >= 64) return launch_fwd_t<T_, D, 4, 2, 64, CAUSAL, SPLIT>(p, st);
+  else return launch_fwd_t<T_, D, 4, 1, 32, CAUSAL, SPLIT>(p, st);
+}
+
+template <int T_, bool CAUSAL, bool SPLIT>
+static hipError_t launch_fwd_c(const FwdParams& p, hipStream_t st) {
+  switch (p.d) {
+    case 16: return launch_fwd_d<T_, 16, CAUSAL, SPLIT>(p, st);
+    case 32: return launch_fwd_d<T_, 32, CAUSAL, SPLIT>(p, st);
+    case 64: return launch_fwd_d<T_, 64, CAUSAL, SPLIT>(p, st);
+    default: return launch_fwd_d<T_, 128, CAUSAL, SPLIT>(p, st);
+  }
+}
+
+template <int T_>
+static hipError_t launch_fwd_dt(const FwdParams& p, bool causal, bool split, hipStream_t st) {
+  if (causal) return split ? launch_fwd_c<T_, true, true>(p, st) : launch_fwd_c<T_, true, false>(p, st);
+  return split ? launch_fwd_c<T_, false, true>(p, st) : launch_fwd_c<T_, false, false>(p, st);
+}
+
+hipError_t launch_fwd(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st) {
+  return dtype == kBF16 ? launch_fwd_dt<kBF16>(p, causal, split, st)
+                        : launch_fwd_dt<kFP16>(p, causal, split, st);
+}
+
+int fwd_rows_per_block(int d) { return d >= 64 ? 4 * 2 * 32 : 4 * 1 * 32; }
+
+template <int T_>
+static hipError_t launch_combine_t(const CombineParams& p, hipStream_t st) {
+  const int64_t grid = (int64_t)p.b * p.h * p.s_q;
+  switch (p.d) {
+    case 16: hipLaunchKernelGGL((combine_kernel<T_, 16>), dim3((unsigned)grid), dim3(256), 0, st, p); break;
+    case 32: hipLaunchKernelGGL((combine_kernel<T_, 32>), dim3((unsigned)grid), dim3(256), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((combine_kernel<T_, 64>), dim3((unsigned)grid), dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((combine_kernel<T_, 128>), dim3((unsigned)grid), dim3(256), 0, st, p); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t st) {
+  return dtype == kBF16 ? launch_combine_t<kBF16>(p, st) : launch_combine_t<kFP16>(p, st);
+}
+
+}  // namespace attn

@@ -1,0 +1,146 @@
+/*
+ * attn.h - exact attention forward for AMD MI355X (gfx950): the C ABI.
+ *
+ * What is computed
+ *   For every batch entry b, head h and query row i:
+ *     S_ij  = softmax_scale * sum_c Q[b,i,h,c] * K[b,j,h,c]     (j visible to i)
+ *     O[b,i,h,:] = sum_j softmax_j(S_i.) * V[b,j,h,:]
+ *     LSE[b,h,i] = ln sum_j exp(S_ij)                            (natural log, fp32)
+ *   This is the standard attention of "LLM Lab Notes 07: Why FlashAttention Is
+ *   Fast" (section 2), evaluated tile by tile with the online-softmax rescale of
+ *   section 3.3 so that S never reaches device memory (sections 3.1 and 3.2).
+ *   The result equals the plain definition up to floating-point rounding.
+ *
+ * Readings fixed by this library where the pages are silent
+ *   - causal != 0 masks with bottom-right alignment: query i sees key j iff
+ *     j <= i + (s_k - s_q).  With s_q == s_k this is the lower triangle; a
+ *     one-row decode query sees the whole cache.
+ *   - a query row that sees no key gets O = 0 and LSE = -inf.
+ *   - O is rounded to the input dtype (round to nearest even); LSE is fp32.
+ *   - softmax_scale is explicit (the pages use 1/sqrt(d)); any finite value,
+ *     zero and negative values included, is accepted.
+ *
+ * Layout
+ *   Q is (b, s_q, h, d); K, V are (b, s_k, h, d); O is (b, s_q, h, d): the
+ *   (batch, seq, heads, dim) order that flash_attn_func consumes in Lab Notes 07
+ *   section 2.  The d dimension is contiguous (stride 1).  The other three
+ *   dimensions take arbitrary non-negative element strides (b, s, h order), each
+ *   a multiple of 8 elements, so flattened (b, s, h*d) tensors and views are
+ *   accepted without copies.  Base pointers must be 16-byte aligned.  LSE is a
+ *   dense fp32 array (b, h, s_q).
+ *
+ * Flash-decoding (flash-attention issue #1248, "where is flash decoding second
+ * stage (reduce) code?")
+ *   attn_fwd_splitkv cuts the keys into num_splits contiguous ranges, split i
+ *   covering keys [floor(i*s_k/n), floor((i+1)*s_k/n)), and writes for every
+ *   split the partial output O_i (normalised within the split, fp32) and LSE_i.
+ *   attn_combine reduces them as the issue's reply describes:
+ *     LSE = log sum_i exp(LSE_i),  O = sum_i exp(LSE_i - LSE) * O_i,
+ *   with max_i LSE_i subtracted before exponentiating.  attn_num_splits picks
+ *   the split count from the device's compute-unit count: it splits only when
+ *   b*h*(query row blocks) leaves compute units idle, as the same reply
+ *   explains for the library's own heuristic.
+ *
+ * Ownership and threading
+ *   The caller allocates every buffer (device memory) and keeps it alive until
+ *   the work enqueued on `stream` has finished.  The library allocates nothing,
+ *   keeps no pointer after a call returns, and enqueues kernels asynchronously
+ *   on `stream` (a hipStream_t; NULL means the default stream).  Calls are
+ *   thread-safe: the only state is a per-device cache of the compute-unit count
+ *   and architecture, filled once.
+ *
+ * Errors
+ *   Every argument is checked on the host before anything is launched.  On any
+ *   error nothing is launched and no output is written; the status says why.
+ *   Checks run in this order: NULL pointers, dtype, shape, head dim, layout,
+ *   scale, split count, then the device.  A failed launch returns
+ *   ATTN_E_LAUNCH.  Faults inside a kernel surface at the caller's next
+ *   synchronisation, as for any asynchronous GPU work.
+ */
+#ifndef EXACT_ATTN_H
+#define EXACT_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_NULL = -1,    /* a required pointer (or the args struct) is NULL */
+  ATTN_E_DTYPE = -2,   /* dtype is not ATTN_FP16 / ATTN_BF16 */
+  ATTN_E_SHAPE = -3,   /* b, h, s_q or s_k < 1, or a size beyond the limits below */
+  ATTN_E_HEADDIM = -4, /* d not in {16, 32, 64, 128}; inputs are never padded */
+  ATTN_E_LAYOUT = -5,  /* misaligned pointer, negative stride, or a stride that is
+                          not a multiple of 8 elements */
+  ATTN_E_SCALE = -6,   /* softmax_scale is NaN or infinite */
+  ATTN_E_SPLITS = -7,  /* num_splits outside [1, min(s_k, ATTN_MAX_SPLITS)] */
+  ATTN_E_DEVICE = -8,  /* no HIP device, or the current device is not gfx950 */
+  ATTN_E_LAUNCH = -9   /* the kernel launch itself failed */
+} attn_status;
+
+typedef enum { ATTN_FP16 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+#define ATTN_MAX_SPLITS 256
+/* Size limits: b*h <= 2^24, s_q and s_k <= 2^24. */
+#define ATTN_MAX_BH (1 << 24)
+#define ATTN_MAX_SEQ (1 << 24)
+
+typedef struct {
+  int32_t dtype;        /* attn_dtype of Q, K, V and O */
+  int32_t causal;       /* 0: every key visible; 1: bottom-right causal mask */
+  int64_t b, s_q, s_k, h, d;
+  const void *q;        /* device pointer, (b, s_q, h, d) */
+  const void *k;        /* device pointer, (b, s_k, h, d) */
+  const void *v;        /* device pointer, (b, s_k, h, d) */
+  void *o;              /* device pointer, (b, s_q, h, d), written */
+  float *lse;           /* device pointer, dense (b, h, s_q) fp32, written;
+                           may be NULL in attn_fwd to skip it; unused by
+                           attn_fwd_splitkv */
+  int64_t q_stride[3];  /* element strides of Q for (b, s, h) */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];  /* unused by attn_fwd_splitkv */
+  float softmax_scale;
+} attn_args;
+
+/* Fused forward (Lab Notes 07 sections 3.1-3.3): O and LSE in one kernel. */
+attn_status attn_fwd(const attn_args *args, void *stream);
+
+/* Split count for flash-decoding on `device` (issue #1248): 1 when
+ * b*h*ceil(s_q/rows_per_block) already covers the compute units, otherwise
+ * enough splits to give each compute unit about two work-groups, capped by
+ * ceil(s_k/256) and ATTN_MAX_SPLITS.  Writes the count to *n_out. */
+attn_status attn_num_splits(int64_t b, int64_t h, int64_t s_q, int64_t s_k, int64_t d,
+                            int device, int32_t *n_out);
+
+/* The same heuristic for an explicit compute-unit count; touches no device. */
+attn_status attn_num_splits_for(int64_t b, int64_t h, int64_t s_q, int64_t s_k,
+                                int64_t d, int32_t num_cus, int32_t *n_out);
+
+/* First stage of flash-decoding (issue #1248): per split i, the attention of
+ * every query over the keys of split i only.  Writes
+ *   o_part  : dense fp32 [num_splits, b, h, s_q, d], O_i normalised within split i
+ *   lse_part: dense fp32 [num_splits, b, h, s_q], natural-log LSE_i
+ * A row that sees no key of a split gets O_i = 0 and LSE_i = -inf.
+ * args->o, args->o_stride and args->lse are ignored. */
+attn_status attn_fwd_splitkv(const attn_args *args, int32_t num_splits,
+                             float *o_part, float *lse_part, void *stream);
+
+/* Second stage (issue #1248's reduce): combine num_splits partials (layouts as
+ * written by attn_fwd_splitkv) into O (dtype, (b, s_q, h, d) with element strides
+ * o_stride for (b, s, h), d contiguous) and LSE (dense fp32 (b, h, s_q); may be
+ * NULL).  A row whose LSE_i are all -inf gets O = 0 and LSE = -inf. */
+attn_status attn_combine(int32_t num_splits, int64_t b, int64_t h, int64_t s_q, int64_t d,
+                         const float *o_part, const float *lse_part, int32_t dtype,
+                         void *o, const int64_t o_stride[3], float *lse, void *stream);
+
+/* Static, human-readable text for a status code. */
+const char *attn_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTN_H */

@@ -1,0 +1,185 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol the header
+declares, its struct mirror matches the C layout, argument validation returns the
+documented status before anything is launched, and the split heuristic behaves.
+
+None of these calls reaches a kernel launch: every argument set below fails a
+host-side check first (fake pointers are never dereferenced).
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import exact_attention_64_amd as ea
+from exact_attention_64_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:attn_status|const char \*)\s*(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    assert set(names) == set(ea.EXPORTS), names
+    L = ea.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stddef.h>
+#include <stdio.h>
+#include "attn.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(attn_args), offsetof(attn_args, b),
+         offsetof(attn_args, q), offsetof(attn_args, lse), offsetof(attn_args, q_stride),
+         offsetof(attn_args, o_stride), offsetof(attn_args, softmax_scale), sizeof(attn_status));
+  return 0;
+}
+''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    A = _lib.AttnArgs
+    want = [ctypes.sizeof(A), A.b.offset, A.q.offset, A.lse.offset, A.q_stride.offset,
+            A.o_stride.offset, A.softmax_scale.offset, 4]
+    assert got == want
+
+
+def _args(**kw):
+    a = _lib.AttnArgs()
+    a.dtype, a.causal = _lib.ATTN_BF16, 0
+    a.b, a.s_q, a.s_k, a.h, a.d = 2, 64, 64, 4, 128
+    a.q = a.k = a.v = a.o = FAKE
+    a.lse = FAKE
+    s = _lib.I64x3(64 * 4 * 128, 4 * 128, 128)
+    a.q_stride = a.k_stride = a.v_stride = a.o_stride = s
+    a.softmax_scale = 0.125
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+BAD = [
+    ("null_q", dict(q=None), -1),
+    ("null_k", dict(k=None), -1),
+    ("null_o", dict(o=None), -1),
+    ("dtype", dict(dtype=7), -2),
+    ("b0", dict(b=0), -3),
+    ("s_k0", dict(s_k=0), -3),
+    ("h_neg", dict(h=-1), -3),
+    ("s_q_huge", dict(s_q=(1 << 24) + 1), -3),
+    ("headdim_8", dict(d=8), -4),
+    ("headdim_96", dict(d=96), -4),
+    ("headdim_256", dict(d=256), -4),
+    ("misaligned_q", dict(q=FAKE + 8), -5),
+    ("misaligned_o", dict(o=FAKE + 2), -5),
+    ("stride_not_mult8", dict(k_stride=_lib.I64x3(8 * 64 * 128, 4 * 128 + 4, 128)), -5),
+    ("stride_negative", dict(v_stride=_lib.I64x3(-64 * 4 * 128, 4 * 128, 128)), -5),
+    ("scale_nan", dict(softmax_scale=float("nan")), -6),
+    ("scale_inf", dict(softmax_scale=float("inf")), -6),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BAD, ids=[b[0] for b in BAD])
+def test_fwd_validation(name, kw, code):
+    a = _args(**kw)
+    assert ea.lib().attn_fwd(ctypes.byref(a), None) == code
+
+
+def test_fwd_null_args():
+    assert ea.lib().attn_fwd(None, None) == -1
+
+
+@pytest.mark.parametrize("n,code", [(0, -7), (-3, -7), (257, -7), (65, -7)])
+def test_splitkv_split_range(n, code):
+    a = _args(s_k=64)
+    assert ea.lib().attn_fwd_splitkv(ctypes.byref(a), n, ctypes.c_void_p(FAKE),
+                                     ctypes.c_void_p(FAKE), None) == code
+
+
+def test_splitkv_null_partials_and_alignment():
+    a = _args()
+    L = ea.lib()
+    assert L.attn_fwd_splitkv(ctypes.byref(a), 2, None, ctypes.c_void_p(FAKE), None) == -1
+    assert L.attn_fwd_splitkv(ctypes.byref(a), 2, ctypes.c_void_p(FAKE + 4),
+                              ctypes.c_void_p(FAKE), None) == -5
+    # o / o_stride are not used by the split kernel: a NULL o is accepted by validation
+    # (the call then stops at an invalid dtype, still before any launch)
+    b = _args(o=None, dtype=5)
+    assert L.attn_fwd_splitkv(ctypes.byref(b), 2, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                              None) == -2
+
+
+def test_combine_validation():
+    L = ea.lib()
+    s = (ctypes.c_int64 * 3)(16 * 128, 16 * 128, 128)
+    F = ctypes.c_void_p(FAKE)
+    assert L.attn_combine(4, 1, 16, 1, 128, None, F, 1, F, s, F, None) == -1
+    assert L.attn_combine(4, 1, 16, 1, 128, F, F, 3, F, s, F, None) == -2
+    assert L.attn_combine(4, 0, 16, 1, 128, F, F, 1, F, s, F, None) == -3
+    assert L.attn_combine(4, 1, 16, 1, 48, F, F, 1, F, s, F, None) == -4
+    assert L.attn_combine(4, 1, 16, 1, 128, ctypes.c_void_p(FAKE + 4), F, 1, F, s, F, None) == -5
+    assert L.attn_combine(0, 1, 16, 1, 128, F, F, 1, F, s, F, None) == -7
+    assert L.attn_combine(300, 1, 16, 1, 128, F, F, 1, F, s, F, None) == -7
+
+
+def test_status_strings():
+    for code in range(-9, 1):
+        text = ea.status_str(code)
+        assert text and text != "unknown status"
+    assert ea.status_str(-42) == "unknown status"
+
+
+def test_num_splits_device_error():
+    n = ctypes.c_int32(0)
+    assert ea.lib().attn_num_splits(1, 16, 1, 32768, 128, 999, ctypes.byref(n)) == -8
+
+
+# --------------------------------------------------------- heuristic ----
+
+def test_heuristic_no_split_with_enough_work():
+    # issue #1248: 8 batches x 48 heads = 384 pieces of work already cover the
+    # compute units, so the heuristic does not split.
+    for s_q in (1, 4, 10):
+        assert ea.attn_num_splits_for(8, 48, s_q, 4096, 128, 256) == 1
+    assert ea.attn_num_splits_for(4, 32, 512, 512, 128, 256) == 1
+
+
+def test_heuristic_splits_small_decode():
+    n = ea.attn_num_splits_for(1, 16, 1, 32768, 128, 256)
+    assert 16 <= n <= 256
+    # split count never exceeds what keeps >= 64 keys per split, nor the cap
+    assert ea.attn_num_splits_for(1, 1, 1, 100, 128, 256) <= 2
+    assert ea.attn_num_splits_for(1, 1, 1, 10 ** 6, 128, 1024) <= 256
+
+
+def test_heuristic_monotone_in_work():
+    prev = 10 ** 9
+    for bh in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512):
+        n = ea.attn_num_splits_for(1, bh, 1, 65536, 128, 256)
+        assert n <= prev
+        prev = n
+    assert prev == 1
+
+
+def test_heuristic_validation():
+    n = ctypes.c_int32()
+    L = ea.lib()
+    assert L.attn_num_splits_for(1, 1, 1, 10, 128, 256, None) == -1
+    assert L.attn_num_splits_for(0, 1, 1, 10, 128, 256, ctypes.byref(n)) == -3
+    assert L.attn_num_splits_for(1, 1, 1, 10, 100, 256, ctypes.byref(n)) == -4
+    assert L.attn_num_splits_for(1, 1, 1, 10, 128, 0, ctypes.byref(n)) == -8

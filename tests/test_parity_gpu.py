@@ -1,0 +1,290 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the float64 CPU oracle.
+
+Both sides get the same seeded, dtype-rounded inputs (workloads.make_qkv).
+Tolerances: max-abs 5e-3 (fp16) / 2e-2 (bf16) on O, 1e-3 on LSE.  Long causal
+prefill is checked on a seeded sample of query rows per head.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import exact_attention_64_amd as ea
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"fp16": 5e-3, "bf16": 2e-2}
+TOL_LSE = 1e-3
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def upload(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+def host64(*ts):
+    """Exact float64 copies of the dtype-rounded inputs, for the oracle."""
+    return [t.to(torch.float64).numpy() for t in ts]
+
+
+def check(O, L, O_ref, L_ref, dtype, what=""):
+    O = f64(O)
+    L = f64(L)
+    fin = np.isfinite(L_ref)
+    assert np.array_equal(np.isfinite(L), fin), f"{what}: -inf rows differ"
+    assert np.all(L[~fin] == -np.inf)
+    eo = np.abs(O - O_ref).max() if O.size else 0.0
+    el = np.abs(L[fin] - L_ref[fin]).max() if fin.any() else 0.0
+    assert np.all(np.isfinite(O)), f"{what}: non-finite O"
+    assert eo <= TOL_O[dtype], f"{what}: max |O - O_ref| = {eo:.3e}"
+    assert el <= TOL_LSE, f"{what}: max |LSE - LSE_ref| = {el:.3e}"
+    return eo, el
+
+
+def run_fwd(q, k, v, scale, causal):
+    qd, kd, vd = upload(q, k, v)
+    O, L = ea.attn_fwd(qd, kd, vd, softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return O, L
+
+
+SMALL = [
+    # dtype, b, s_q, s_k, h, d  -- several tiles plus ragged tails
+    ("bf16", 2, 300, 333, 3, 128),
+    ("fp16", 2, 300, 333, 3, 128),
+    ("bf16", 1, 517, 517, 2, 64),
+    ("fp16", 3, 129, 257, 2, 64),
+    ("bf16", 2, 200, 161, 3, 32),
+    ("fp16", 2, 97, 130, 4, 32),
+    ("bf16", 2, 150, 150, 5, 16),
+    ("fp16", 1, 33, 65, 3, 16),
+    ("bf16", 1, 1, 700, 4, 128),   # one query row (decode shape) through the fused kernel
+    ("fp16", 1, 700, 5, 2, 128),   # fewer keys than rows: causal rows at the top see nothing
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", SMALL, ids=[f"{c[0]}-b{c[1]}-q{c[2]}-k{c[3]}-h{c[4]}-d{c[5]}" for c in SMALL])
+def test_fwd_small(case, causal):
+    dt, b, s_q, s_k, h, d = case
+    say("attn_fwd", case, "causal", causal, "seed 42")
+    q, k, v = workloads.make_qkv(b, s_q, s_k, h, d, dt, seed=42)
+    scale = 1 / math.sqrt(d)
+    O, L = run_fwd(q, k, v, scale, causal)
+    O_ref, L_ref = oracle.attention(*host64(q, k, v), scale, causal)
+    check(O, L, O_ref, L_ref, dt, str(case))
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3"])
+def test_fwd_workloads_full(name):
+    w = workloads.WORKLOADS[name]
+    say("attn_fwd", name, w.note)
+    q, k, v = workloads.make_workload(w)
+    O, L = run_fwd(q, k, v, w.scale, w.causal)
+    O_ref, L_ref = oracle.attention(*host64(q, k, v), w.scale, w.causal)
+    check(O, L, O_ref, L_ref, w.dtype, name)
+
+
+def test_fwd_long_causal_sampled():
+    w = workloads.WORKLOADS["C5"]
+    say("attn_fwd", "C5", w.note, "sampled rows", w.sample_rows)
+    q, k, v = workloads.make_workload(w)
+    O, L = run_fwd(q, k, v, w.scale, w.causal)
+    rows = workloads.sample_rows(w.s_q, w.sample_rows, w.h, seed=42)
+    O_ref, L_ref = oracle.attention_rows(*host64(q, k, v), w.scale, w.causal, rows)
+    Ocpu = O.cpu()
+    Lcpu = L.cpu()
+    r = torch.tensor(rows)  # (h, n)
+    O_s = torch.stack([Ocpu[:, r[hi], hi, :] for hi in range(w.h)], dim=1)  # (b, h, n, d)
+    L_s = torch.stack([Lcpu[:, hi, r[hi]] for hi in range(w.h)], dim=1)
+    check(O_s, L_s, O_ref, L_ref, w.dtype, "C5 sampled")
+    # rows past the sample still obey invariants: finite, |O| bounded by max |V|
+    assert torch.isfinite(Ocpu.float()).all()
+    assert (Ocpu.float().abs().amax() <= v.float().abs().amax() + 1e-2)
+
+
+def test_decode_workload_split_and_combine():
+    w = workloads.WORKLOADS["C4"]
+    q, k, v = workloads.make_workload(w)
+    qd, kd, vd = upload(q, k, v)
+    n = ea.attn_num_splits(w.b, w.h, w.s_q, w.s_k, w.d)
+    say("attn_fwd_splitkv + attn_combine", "C4", w.note, "splits", n)
+    assert n > 1
+    O, L = ea.attn_decode(qd, kd, vd, num_splits=n, softmax_scale=w.scale)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(*host64(q, k, v), w.scale, False)
+    check(O, L, O_ref, L_ref, w.dtype, "C4 split")
+    say("attn_fwd", "C4 unsplit")
+    O1, L1 = ea.attn_fwd(qd, kd, vd, softmax_scale=w.scale)
+    torch.cuda.synchronize()
+    check(O1, L1, O_ref, L_ref, w.dtype, "C4 fused")
+
+
+SPLIT_CASES = [
+    ("bf16", 1, 1, 1000, 4, 128, 7),
+    ("bf16", 2, 3, 257, 3, 64, 5),
+    ("fp16", 1, 130, 300, 2, 128, 3),
+    ("fp16", 2, 50, 50, 16, 16, 50),    # one key per split
+    ("bf16", 1, 64, 64, 2, 32, 64),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[f"{c[0]}-b{c[1]}-q{c[2]}-k{c[3]}-n{c[6]}" for c in SPLIT_CASES])
+def test_splitkv_partials_and_combine(case, causal):
+    dt, b, s_q, s_k, h, d, n = case
+    say("attn_fwd_splitkv", case, "causal", causal)
+    q, k, v = workloads.make_qkv(b, s_q, s_k, h, d, dt, seed=7)
+    scale = 1 / math.sqrt(d)
+    qd, kd, vd = upload(q, k, v)
+    Op, Lp = ea.attn_fwd_splitkv(qd, kd, vd, num_splits=n, softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    Op_ref, Lp_ref = oracle.attention_split(*host64(q, k, v), scale, causal, oracle.split_bounds(s_k, n))
+    # partials are fp32 but built from a P rounded to the input type: same tolerance
+    Lp_h = f64(Lp)
+    fin = np.isfinite(Lp_ref)
+    assert np.array_equal(np.isfinite(Lp_h), fin)
+    assert np.abs(Lp_h[fin] - Lp_ref[fin]).max() <= TOL_LSE
+    assert np.abs(f64(Op) - Op_ref).max() <= TOL_O[dt]
+    say("attn_combine", case)
+    O, L = ea.attn_combine(Op, Lp, q.dtype)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(*host64(q, k, v), scale, causal)
+    check(O, L, O_ref, L_ref, dt, f"{case} combined")
+    # split + combine agrees with the fused kernel
+    O1, L1 = ea.attn_fwd(qd, kd, vd, softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    assert (O1.float() - O.float()).abs().max().item() <= TOL_O[dt]
+
+
+def test_combine_identical_splits_adds_ln2():
+    say("attn_combine identical splits")
+    g = torch.Generator().manual_seed(3)
+    o = torch.randn((1, 2, 3, 5, 64), generator=g)
+    lse = torch.randn((1, 2, 3, 5), generator=g) * 30
+    Op = torch.cat([o, o]).to(DEV)
+    Lp = torch.cat([lse, lse]).to(DEV)
+    O, L = ea.attn_combine(Op, Lp, torch.float16)
+    torch.cuda.synchronize()
+    assert (L.cpu() - (lse[0] + math.log(2))).abs().max() < 1e-4
+    err = (O.cpu().float().permute(0, 2, 1, 3) - o[0]).abs()
+    assert (err <= o[0].abs() * 2.0 ** -10 + 1e-6).all()
+    # all splits empty: O = 0, LSE = -inf
+    Lp2 = torch.full((3, 1, 2, 5), float("-inf"), device=DEV)
+    Op2 = torch.zeros((3, 1, 2, 5, 16), device=DEV)
+    O2, L2 = ea.attn_combine(Op2, Lp2, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert (O2 == 0).all() and torch.isinf(L2).all() and (L2 < 0).all()
+
+
+# ------------------------------------------------------------ edge cases ----
+
+@pytest.mark.parametrize("d", [16, 128])
+def test_single_key_returns_v(d):
+    say("attn_fwd single key", d)
+    q, k, v = workloads.make_qkv(2, 37, 1, 3, d, "bf16", seed=5)
+    O, L = run_fwd(q, k, v, 0.3, False)
+    assert torch.equal(O.cpu(), v.expand(2, 37, 3, d))  # weight exactly 1
+    ref = 0.3 * torch.einsum("bshd,bhd->bhs", q.double(), k[:, 0].double())
+    assert (L.cpu().double() - ref).abs().max() < TOL_LSE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_q_zero_closed_form(causal):
+    say("attn_fwd Q=0", causal)
+    _, k, v = workloads.make_qkv(1, 80, 200, 2, 128, "bf16", seed=9)
+    q = torch.zeros((1, 80, 2, 128), dtype=torch.bfloat16)
+    O, L = run_fwd(q, k, v, 0.088, causal)
+    off = 200 - 80
+    cnt = np.array([200 if not causal else i + off + 1 for i in range(80)], dtype=np.float64)
+    np.testing.assert_allclose(f64(L)[0, 0], np.log(cnt), atol=1e-5)
+    vm = torch.stack([v[0, :int(c)].double().mean(0) for c in cnt])  # (80, h, d)
+    assert (O[0].cpu().double() - vm).abs().max() < 2e-2
+
+
+def test_scale_zero_and_negative():
+    q, k, v = workloads.make_qkv(1, 70, 90, 2, 64, "fp16", seed=11)
+    for scale in (0.0, -0.125):
+        for causal in (False, True):
+            say("attn_fwd scale", scale, "causal", causal)
+            O, L = run_fwd(q, k, v, scale, causal)
+            O_ref, L_ref = oracle.attention(*host64(q, k, v), scale, causal)
+            check(O, L, O_ref, L_ref, "fp16", f"scale {scale}")
+
+
+def test_large_scores_stay_finite():
+    # Scores far beyond exp's range: without the max subtraction this overflows.
+    say("attn_fwd large scores")
+    q, k, v = workloads.make_qkv(1, 64, 300, 2, 128, "bf16", seed=13)
+    scale = 8.0
+    O, L = run_fwd(q, k, v, scale, False)
+    O_ref, L_ref = oracle.attention(*host64(q, k, v), scale, False)
+    assert np.abs(L_ref).max() > 150
+    # |LSE| is large here, so compare it relative to its size
+    assert torch.isfinite(O).all() and torch.isfinite(L).all()
+    assert np.abs(f64(O) - O_ref).max() <= TOL_O["bf16"]
+    assert np.abs(f64(L) - L_ref).max() <= 1e-5 * np.abs(L_ref).max() + TOL_LSE
+
+
+def test_strided_views_and_no_lse():
+    say("attn_fwd packed qkv views")
+    g = torch.Generator().manual_seed(17)
+    b, s, h, d = 2, 190, 4, 64
+    qkv = torch.randn((b, s, 3, h, d), generator=g).to(torch.bfloat16)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    qkvd = qkv.to(DEV)
+    qd, kd, vd = qkvd[:, :, 0], qkvd[:, :, 1], qkvd[:, :, 2]
+    out_big = torch.zeros((b, s, h, 2 * d), dtype=torch.bfloat16, device=DEV)
+    out = out_big[..., :d]
+    O, L = ea.attn_fwd(qd, kd, vd, softmax_scale=0.125, causal=True, out=out, return_lse=False)
+    torch.cuda.synchronize()
+    assert L is None
+    O_ref, _ = oracle.attention(*host64(q, k, v), 0.125, True)
+    assert np.abs(f64(out) - O_ref).max() <= TOL_O["bf16"]
+    assert (out_big[..., d:] == 0).all()  # the other half of each row is untouched
+
+
+def test_outputs_leave_guard_bands_untouched():
+    say("attn_fwd guard bands")
+    q, k, v = workloads.make_qkv(1, 129, 77, 3, 32, "fp16", seed=19)
+    qd, kd, vd = upload(q, k, v)
+    n_o = q.numel()
+    o_buf = torch.full((n_o + 4096,), 7.0, dtype=torch.float16, device=DEV)
+    l_buf = torch.full((3 * 129 + 1024,), 7.0, dtype=torch.float32, device=DEV)
+    O = o_buf[:n_o].view(q.shape)
+    L = l_buf[:3 * 129].view(1, 3, 129)
+    ea.attn_fwd(qd, kd, vd, causal=True, out=O, lse=L)
+    torch.cuda.synchronize()
+    assert (o_buf[n_o:] == 7.0).all() and (l_buf[3 * 129:] == 7.0).all()
+
+
+def test_deterministic_bitwise():
+    say("attn_fwd determinism")
+    q, k, v = workloads.make_qkv(2, 333, 333, 4, 128, "bf16", seed=23)
+    qd, kd, vd = upload(q, k, v)
+    O1, L1 = ea.attn_fwd(qd, kd, vd, causal=True)
+    O2, L2 = ea.attn_fwd(qd, kd, vd, causal=True)
+    Op1, Lp1 = ea.attn_fwd_splitkv(qd, kd, vd, num_splits=5)
+    Op2, Lp2 = ea.attn_fwd_splitkv(qd, kd, vd, num_splits=5)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+    assert torch.equal(Op1, Op2) and torch.equal(Lp1, Lp2)
+
+
+def test_bad_head_dim_rejected():
+    say("attn_fwd bad head dim on device tensors")
+    q = torch.zeros((1, 8, 2, 48), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ea.AttnError) as e:
+        ea.attn_fwd(q, q, q)
+    assert e.value.status == -4
