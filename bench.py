@@ -1,0 +1,304 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over resident synthetic inputs:
+  * fused prefill  attn_fwd            on the long causal workload
+    (bf16, b=1, s_q=s_k=16384, h=32, d=128), and
+  * flash-decoding attn_fwd_splitkv + attn_combine on the decode workload
+    (bf16, b=1, s_q=1, s_k=32768, h=16, d=128), split count from the
+    compute-unit heuristic.
+``value`` is the prefill throughput in TFLOP/s (algorithmic FLOPs: 4*d per
+visible (query, key) pair).  The decode figure (K+V bytes over the time of both
+decode launches) is reported beside it.  Kernel durations come from HIP events
+recorded on the stream the kernels run on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|decode]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNEL_SOURCES = ["exact_attention_64_amd/csrc/attn_kernels.hip"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.md")
+CPU_ROWS_PER_HEAD = 2048  # seeded query rows per head in the CPU-baseline sample
+
+
+def visible_pairs(w) -> int:
+    if not w.causal:
+        return w.b * w.h * w.s_q * w.s_k
+    off = w.s_k - w.s_q
+    per_head = sum(max(0, min(w.s_k, i + off + 1)) for i in range(w.s_q))
+    return w.b * w.h * per_head
+
+
+def flops(w) -> int:
+    return 4 * w.d * visible_pairs(w)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kind: str):
+    """HBM bytes per launch from the committed counter summary, if it matches the
+    current kernel source; otherwise None."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    m = re.search(r"kernel_hash:\s*(\w+)", text)
+    if not m or m.group(1) != kernel_hash():
+        return None
+    m = re.search(kind + r"_hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    return float(m.group(1)) if m else None
+
+
+def cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """Time the float64 oracle on a bounded sample of the prefill workload: whole
+    heads' worth of seeded query rows until about ``budget_s`` seconds of work."""
+    import numpy as np
+    import oracle
+    import workloads
+
+    import torch
+
+    q, k, v = workloads.make_workload(w)
+    rows_all = workloads.sample_rows(w.s_q, CPU_ROWS_PER_HEAD, w.h, seed=42)
+    done_flops = 0
+    done_rows = 0
+    heads = 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    off = w.s_k - w.s_q
+    for hi in range(w.h):
+        qh, kh, vh = (t[:, :, hi:hi + 1].to(torch.float64).numpy() for t in (q, k, v))
+        t1 = time.perf_counter()
+        oracle.attention_rows(qh, kh, vh, w.scale, w.causal, [rows_all[hi]])
+        elapsed += time.perf_counter() - t1
+        pairs = sum(min(w.s_k, r + off + 1) if w.causal else w.s_k for r in rows_all[hi])
+        done_flops += 4 * w.d * pairs * w.b
+        done_rows += len(rows_all[hi]) * w.b
+        heads += 1
+        if elapsed >= budget_s:
+            break
+    return {
+        "value": round(done_flops / elapsed / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": cpu_threads(),
+        "kind": "oracle",
+        "sample": (f"float64 NumPy oracle, {done_rows} seeded query rows ({len(rows_all[0])} per head, "
+                   f"{heads} of {w.h} heads) of the causal s=16384 workload, each over its full key "
+                   f"prefix; {done_flops / 1e9:.1f} GFLOP in {elapsed:.2f} s"),
+        "seconds": round(elapsed, 3),
+        "extrapolated_full_s": round(elapsed * flops(w) / done_flops, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--no-small", action="store_true", help="skip the per-workload side table")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy five times (reference "
+                         "kernel of known size for scaling HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path: heads (prefill) or the key sequence (decode) would be sharded "
+              "across GPUs, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_64_amd as ea
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calib:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": n, "launches": 5}), flush=True)
+        return
+    W = workloads.WORKLOADS
+    wp, wd = W["C5"], W["C4"]
+    do_p = args.only in ("all", "prefill")
+    do_d = args.only in ("all", "decode")
+
+    # ---- resident inputs and outputs
+    if do_p:
+        qp, kp, vp = (t.to(dev) for t in workloads.make_workload(wp))
+        Op = torch.empty_like(qp)
+        Lp = torch.empty((wp.b, wp.h, wp.s_q), dtype=torch.float32, device=dev)
+    if do_d:
+        qd, kd, vd = (t.to(dev) for t in workloads.make_workload(wd))
+        n_splits = ea.attn_num_splits(wd.b, wd.h, wd.s_q, wd.s_k, wd.d)
+        opart = torch.empty((n_splits, wd.b, wd.h, wd.s_q, wd.d), dtype=torch.float32, device=dev)
+        lpart = torch.empty((n_splits, wd.b, wd.h, wd.s_q), dtype=torch.float32, device=dev)
+        Od = torch.empty_like(qd)
+        Ld = torch.empty((wd.b, wd.h, wd.s_q), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(evs):
+        if do_p:
+            evs[0].record()
+            ea.attn_fwd(qp, kp, vp, wp.scale, wp.causal, out=Op, lse=Lp)
+            evs[1].record()
+        if do_d:
+            evs[2].record()
+            ea.attn_fwd_splitkv(qd, kd, vd, n_splits, wd.scale, False, o_part=opart, lse_part=lpart)
+            evs[3].record()
+            ea.attn_combine(opart, lpart, qd.dtype, out=Od, lse=Ld)
+            evs[4].record()
+
+    for _ in range(args.warmup):
+        step([E() for _ in range(5)])
+    torch.cuda.synchronize()
+
+    events = [[E() for _ in range(5)] for _ in range(args.steps)]
+    t_start, t_end = E(), E()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(events[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = max(ms_total, wall * 1e3) / args.steps
+
+    res = {}
+    if do_p:
+        p_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+        p_tf = flops(wp) / (p_ms * 1e-3) / 1e12
+        res["prefill"] = dict(ms=p_ms, tflops=p_tf)
+    if do_d:
+        s_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+        c_ms = sum(e[3].elapsed_time(e[4]) for e in events) / args.steps
+        d_ms = sum(e[2].elapsed_time(e[4]) for e in events) / args.steps
+        kvb = 2 * 2 * wd.b * wd.s_k * wd.h * wd.d
+        res["decode"] = dict(ms=d_ms, splitkv_ms=s_ms, combine_ms=c_ms, gbs=kvb / (d_ms * 1e-3) / 1e9,
+                             splitkv_gbs=kvb / (s_ms * 1e-3) / 1e9, kv_bytes=kvb, splits=n_splits)
+
+    # ---- side table: the three smaller prefill workloads (median of 20 launches each)
+    side = {}
+    if not args.no_small and args.only == "all":
+        for name in ("C1", "C2", "C3"):
+            w = W[name]
+            q, k, v = (t.to(dev) for t in workloads.make_workload(w))
+            O = torch.empty_like(q)
+            L = torch.empty((w.b, w.h, w.s_q), dtype=torch.float32, device=dev)
+            for _ in range(3):
+                ea.attn_fwd(q, k, v, w.scale, w.causal, out=O, lse=L)
+            ts = []
+            for _ in range(20):
+                a, b = E(), E()
+                a.record()
+                ea.attn_fwd(q, k, v, w.scale, w.causal, out=O, lse=L)
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            ts.sort()
+            med = ts[len(ts) // 2]
+            io = 2 * w.b * w.h * w.d * (2 * w.s_q + 2 * w.s_k) + 4 * w.b * w.h * w.s_q
+            side[name] = dict(workload=w.note, us=round(med * 1e3, 2),
+                              tflops=round(flops(w) / (med * 1e-3) / 1e12, 2),
+                              io_gbs=round(io / (med * 1e-3) / 1e9, 1),
+                              frac_mfma=round(flops(w) / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+            del q, k, v, O, L
+
+    out = {
+        "metric": "attn fwd TFLOP/s (prefill) & decode K/V GB/s, % of MI355X MFMA/HBM peak",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q, k, v rounded to bf16 on the host)",
+    }
+    if do_p:
+        p = res["prefill"]
+        out.update(value=round(p["tflops"], 2), unit="TFLOP/s")
+        out["config"] = {
+            "workload": "causal prefill bf16 b=1 s_q=s_k=16384 h=32 d=128 (attn_fwd)"
+                        + (" + split-KV decode bf16 b=1 s_q=1 s_k=32768 h=16 d=128 "
+                           "(attn_fwd_splitkv + attn_combine)" if do_d else ""),
+            "b": wp.b, "s_q": wp.s_q, "s_k": wp.s_k, "h": wp.h, "d": wp.d, "causal": True,
+        }
+        out["roofline"] = {
+            "bound": "mfma", "achieved": round(p["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4),
+            "traffic": read_traffic("prefill"),
+            "kernel": "fwd_kernel (attn_fwd)", "avg_launch_ms": round(p["ms"], 4),
+            "flops_per_launch": flops(wp),
+        }
+    if do_d:
+        dd = res["decode"]
+        dec = {
+            "value": round(dd["gbs"], 1), "unit": "GB/s", "us": round(dd["ms"] * 1e3, 2),
+            "splitkv_us": round(dd["splitkv_ms"] * 1e3, 2), "combine_us": round(dd["combine_ms"] * 1e3, 2),
+            "splits": dd["splits"], "frac_hbm": round(dd["gbs"] / PEAK_HBM_GBS, 4),
+        }
+        rd = {
+            "bound": "hbm", "achieved": round(dd["splitkv_gbs"], 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(dd["splitkv_gbs"] / PEAK_HBM_GBS, 4),
+            "traffic": read_traffic("decode"), "kernel": "split-KV kernel (attn_fwd_splitkv)",
+            "avg_launch_ms": round(dd["splitkv_ms"], 4), "bytes_per_launch": dd["kv_bytes"],
+        }
+        if do_p:
+            out["decode"] = dec
+            out["roofline_decode"] = rd
+        else:
+            out.update(value=dec["value"], unit="GB/s")
+            out["config"] = {"workload": "split-KV decode bf16 b=1 s_q=1 s_k=32768 h=16 d=128",
+                             "b": wd.b, "s_q": wd.s_q, "s_k": wd.s_k, "h": wd.h, "d": wd.d}
+            out["decode"] = dec
+            out["roofline"] = rd
+    if side:
+        out["other_workloads"] = side
+    if not args.no_cpu and do_p:
+        out["cpu_baseline"] = cpu_baseline(wp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
