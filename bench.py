@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNEL_SOURCES = ["exact_attention_64_amd/csrc/attn_kernels.hip"]
+KERNEL_SOURCES = ["exact_attention_64_amd/csrc/attn_fwd.hip", "exact_attention_64_amd/csrc/attn_decode.hip",
+                  "exact_attention_64_amd/csrc/attn_common.h"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.md")
 CPU_ROWS_PER_HEAD = 2048  # seeded query rows per head in the CPU-baseline sample
 

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libattn.so")
 
-SOURCES = ["attn_api.cpp", "attn_kernels.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_decode.hip", "attn_combine.hip"]
 
 # Packed fp32 VALU instructions are switched off for every HIP translation unit.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -31,7 +31,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build(verbose: bool = False, jobs: int = 2) -> str:
+def build(verbose: bool = False) -> str:
     """Compile every source for gfx950 and link ``libattn.so``. Returns its path."""
     cc = hipcc()
     objs = []

@@ -112,7 +112,7 @@ void fill_params(const attn_args* a, attn::FwdParams* p) {
 }
 
 bool grid_ok(const attn_args* a, int64_t n_splits) {
-  const int64_t bm = attn::fwd_rows_per_block((int)a->d);
+  const int64_t bm = attn::fwd_rows_per_block((int)a->d, (int)a->s_q);
   const int64_t grid = ceil_div(a->s_q, bm) * a->b * a->h * n_splits;
   return grid <= 0x7fffffff;
 }
@@ -157,11 +157,12 @@ attn_status attn_num_splits_for(int64_t b, int64_t h, int64_t s_q, int64_t s_k, 
   if (!headdim_ok(d)) return ATTN_E_HEADDIM;
   if (num_cus < 1) return ATTN_E_DEVICE;
   // Parallel work without splitting: one work-group per (b, h, query row block).
-  const int64_t work = b * h * ceil_div(s_q, attn::fwd_rows_per_block((int)d));
+  const int64_t work = b * h * ceil_div(s_q, attn::fwd_rows_per_block((int)d, (int)s_q));
   int64_t n = 1;
   if (work < num_cus) {
-    // About two work-groups per compute unit, each split keeping >= 64 keys.
-    n = ceil_div(2 * (int64_t)num_cus, work);
+    // About one work-group per compute unit (measured best for the one-row
+    // decode kernel: fewer, longer key streams), each split keeping >= 64 keys.
+    n = ceil_div((int64_t)num_cus, work);
     n = n < ceil_div(s_k, 64) ? n : ceil_div(s_k, 64);
     n = n < ATTN_MAX_SPLITS ? n : ATTN_MAX_SPLITS;
     n = n < 1 ? 1 : n;

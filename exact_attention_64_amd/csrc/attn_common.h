@@ -1,0 +1,66 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, the per-dtype
+// MFMA flavour and rounding, and cross-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_internal.h"
+
+namespace attn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From& x) {
+  static_assert(sizeof(To) == sizeof(From), "size");
+  return __builtin_bit_cast(To, x);
+}
+
+// Per-dtype pieces: the MFMA flavour and float -> storage rounding (nearest even).
+template <int DT> struct Ty;
+template <> struct Ty<kBF16> {
+  static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack2(float x, float y) {
+    bf16x2_t v = {(__bf16)x, (__bf16)y};
+    return bitcast<unsigned>(v);
+  }
+  static __device__ __forceinline__ unsigned short one(float x) { return bitcast<unsigned short>((__bf16)x); }
+};
+template <> struct Ty<kFP16> {
+  static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<f16x8_t>(a), bitcast<f16x8_t>(b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack2(float x, float y) {
+    f16x2_t v = {(_Float16)x, (_Float16)y};
+    return bitcast<unsigned>(v);
+  }
+  static __device__ __forceinline__ unsigned short one(float x) { return bitcast<unsigned short>((_Float16)x); }
+};
+
+// Maximum of a value and its partner lane (lane ^ 32), in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace attn

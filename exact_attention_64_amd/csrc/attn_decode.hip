@@ -1,0 +1,218 @@
+// One-query-row (decode) split-KV kernel for gfx950 (MI355X): flash-decoding's
+// first stage (flash-attention issue #1248) as a memory-streaming pass.
+#include "attn_common.h"
+
+namespace attn {
+
+// ---------------------------------------------------------------------------
+// One-query-row forward (decode), the flash-decoding first stage of issue #1248
+// for s_q == 1.  The pass is bound by reading K and V once, so it runs on the
+// vector ALUs with wide streaming loads and no LDS staging; matrix cores would
+// idle on a single query row (the issue's reply makes the same point: decode
+// speed is close to a memory copy, so spare compute does not matter).
+//
+// Work-group = NWV waves on one (b, h, split); wave w takes a contiguous quarter
+// of the split's keys.  Lane layout: a key row (D elements) is read by LPH = D/8
+// lanes, 16 bytes each, so one wave load covers KPI = 64/LPH consecutive keys.
+// Each group of LPH lanes ("slot") runs its own online softmax over the keys it
+// reads; the NWV*KPI slot states are merged through LDS at the end with the same
+// max-subtracted rule as the combine.
+template <int LPH>
+__device__ __forceinline__ float slot_sum(float x) {
+  // all-reduce over the LPH consecutive lanes of a slot (DPP within a row of 16)
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+  if (LPH >= 4) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // lane ^ 2
+  if (LPH >= 8) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // half mirror
+  if (LPH >= 16) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // mirror
+  return x;
+}
+
+template <int T_> struct Dot;
+template <> struct Dot<kBF16> {
+  static __device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(a[i]), bitcast<bf16x2_t>(b[i]), acc, false);
+    return acc;
+  }
+  static __device__ __forceinline__ void unpack8(u32x4_t a, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(a[i] << 16);
+      f[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Dot<kFP16> {
+  static __device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2(bitcast<f16x2_t>(a[i]), bitcast<f16x2_t>(b[i]), acc, false);
+    return acc;
+  }
+  static __device__ __forceinline__ void unpack8(u32x4_t a, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2_t h = bitcast<f16x2_t>(a[i]);
+      f[2 * i] = (float)h[0];
+      f[2 * i + 1] = (float)h[1];
+    }
+  }
+};
+
+template <int T_, int D, int NWV, bool SPLIT>
+__global__ __launch_bounds__(NWV * 64) void decode_kernel(const FwdParams p) {
+  using Tt = Ty<T_>;
+  using Dt = Dot<T_>;
+  constexpr int LPH = D / 8;        // lanes per key row
+  constexpr int KPI = 64 / LPH;     // keys per wave load
+  constexpr int U = kDecodeBatch;   // wave loads per tensor in one batch
+  constexpr int NS = NWV * KPI;     // slot states merged at the end
+
+  __shared__ float red_m[NS], red_l[NS];
+  __shared__ __attribute__((aligned(16))) float red_o[NS][D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int slot = lane / LPH;
+  const int dc = lane % LPH;
+  const int split = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int bb = bh / p.h;
+  const int hh = bh - bb * p.h;
+
+  int k_lo = 0, k_hi = p.s_k;
+  if (SPLIT) {
+    k_lo = (int)(((int64_t)split * p.s_k) / p.n_splits);
+    k_hi = (int)(((int64_t)(split + 1) * p.s_k) / p.n_splits);
+  }
+  const int ws = k_lo + (int)(((int64_t)(k_hi - k_lo) * wave) / NWV);
+  const int we = k_lo + (int)(((int64_t)(k_hi - k_lo) * (wave + 1)) / NWV);
+
+  u32x4_t q = {0u, 0u, 0u, 0u};
+  if (!p.zero_q) {
+    q = *(const u32x4_t*)((const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2] + dc * 8);
+    if (p.neg_q) q ^= 0x80008000u;
+  }
+  const unsigned short* __restrict__ Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hh * p.ks[2] + dc * 8;
+  const unsigned short* __restrict__ Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hh * p.vs[2] + dc * 8;
+  const int64_t ksr = p.ks[1], vsr = p.vs[1];
+  const float c = p.scale_log2;
+
+  float m = -INFINITY, l = 0.f;
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+
+  // Two register buffers, used alternately by a loop unrolled twice, so that the
+  // loads of one batch are in flight while the other is consumed (indices stay
+  // compile-time constants and the buffers stay in registers).
+  u32x4_t kb0[U], vb0[U], kb1[U], vb1[U];
+  auto load = [&](u32x4_t (&kb)[U], u32x4_t (&vb)[U], int j0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * KPI + slot;
+      u32x4_t xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+      if (j < we) {
+        xk = __builtin_nontemporal_load((const u32x4_t*)(Kg + (int64_t)j * ksr));
+        xv = __builtin_nontemporal_load((const u32x4_t*)(Vg + (int64_t)j * vsr));
+      }
+      kb[u] = xk;
+      vb[u] = xv;
+    }
+  };
+  auto consume = [&](const u32x4_t (&kb)[U], const u32x4_t (&vb)[U], int j0) {
+    float s[U];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      s[u] = slot_sum<LPH>(Dt::dot8(q, kb[u], 0.f));
+      if (j0 + u * KPI + slot >= we) s[u] = -INFINITY;
+      mx = fmaxf(mx, s[u]);
+    }
+    const float m_new = fmaxf(m, mx * c);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float pu = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u], c, -m_use));
+      l += pu;
+      float f[8];
+      Dt::unpack8(vb[u], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(pu, f[e], o[e]);
+    }
+    m = m_new;
+  };
+  constexpr int STEP = U * KPI;
+  if (ws < we) load(kb0, vb0, ws);
+  for (int j0 = ws; j0 < we; j0 += 2 * STEP) {
+    if (j0 + STEP < we) load(kb1, vb1, j0 + STEP);
+    consume(kb0, vb0, j0);
+    if (j0 + STEP >= we) break;
+    if (j0 + 2 * STEP < we) load(kb0, vb0, j0 + 2 * STEP);
+    consume(kb1, vb1, j0 + STEP);
+  }
+
+  // merge the NS slot states
+  const int st = wave * KPI + slot;
+  if (dc == 0) {
+    red_m[st] = m;
+    red_l[st] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red_o[st][dc * 8 + e] = o[e];
+  __syncthreads();
+  if (tid < D / 4) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) M = fmaxf(M, red_m[i]);
+    const float Ms = M == -INFINITY ? 0.f : M;
+    float L = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const float w = __builtin_amdgcn_exp2f(red_m[i] - Ms);
+      L += w * red_l[i];
+      acc += w * *(const f32x4_t*)&red_o[i][tid * 4];
+    }
+    const bool has = L > 0.f;
+    const float inv = has ? 1.f / L : 0.f;
+    const float lse = has ? (Ms + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
+    acc *= inv;
+    if (SPLIT) {
+      const int64_t rowi = ((int64_t)split * p.b + bb) * p.h + hh;  // s_q == 1
+      *(f32x4_t*)(p.o_part + rowi * D + tid * 4) = acc;
+      if (tid == 0) p.lse_part[rowi] = lse;
+    } else {
+      unsigned short* op = (unsigned short*)p.o + (int64_t)bb * p.os[0] + (int64_t)hh * p.os[2];
+      u32x2_t x = {Tt::pack2(acc[0], acc[1]), Tt::pack2(acc[2], acc[3])};
+      *(u32x2_t*)(op + tid * 4) = x;
+      if (tid == 0 && p.lse) p.lse[(int64_t)bb * p.h + hh] = lse;
+    }
+  }
+}
+
+template <int T_, bool SPLIT>
+static hipError_t launch_decode_t(const FwdParams& p, hipStream_t st) {
+  constexpr int NWV = kDecodeWaves;
+  const dim3 grid((unsigned)p.n_splits, (unsigned)(p.b * p.h));
+  switch (p.d) {
+    case 16: hipLaunchKernelGGL((decode_kernel<T_, 16, NWV, SPLIT>), grid, dim3(NWV * 64), 0, st, p); break;
+    case 32: hipLaunchKernelGGL((decode_kernel<T_, 32, NWV, SPLIT>), grid, dim3(NWV * 64), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((decode_kernel<T_, 64, NWV, SPLIT>), grid, dim3(NWV * 64), 0, st, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<T_, 128, NWV, SPLIT>), grid, dim3(NWV * 64), 0, st, p); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const FwdParams& p, int dtype, bool split, hipStream_t st) {
+  if (dtype == kBF16) return split ? launch_decode_t<kBF16, true>(p, st) : launch_decode_t<kBF16, false>(p, st);
+  return split ? launch_decode_t<kFP16, true>(p, st) : launch_decode_t<kFP16, false>(p, st);
+}
+
+}  // namespace attn

@@ -1,4 +1,4 @@
-// Exact attention forward kernels for gfx950 (MI355X).
+// Fused exact attention forward (prefill) kernel for gfx950 (MI355X).
 //
 // The fused kernel follows "LLM Lab Notes 07: Why FlashAttention Is Fast":
 // the score matrix is produced one tile at a time and never stored (section 3.1,
@@ -18,66 +18,9 @@
 //   P            : exp2 of the scaled scores minus the running maximum (log2(e)
 //                  folded into the scale), rounded to the input type.
 //   O^T += V^T P^T : MFMA; V^T fragments come from ds_read_b64_tr_b16.
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include "attn_internal.h"
+#include "attn_common.h"
 
 namespace attn {
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
-typedef __attribute__((ext_vector_type(4))) short s16x4_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-typedef __attribute__((ext_vector_type(16))) float f32x16_t;
-typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
-typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
-
-#define LDS_AS __attribute__((address_space(3)))
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-template <typename To, typename From>
-__device__ __forceinline__ To bitcast(const From& x) {
-  static_assert(sizeof(To) == sizeof(From), "size");
-  return __builtin_bit_cast(To, x);
-}
-
-// Per-dtype pieces: the MFMA flavour and float -> storage rounding (nearest even).
-template <int DT> struct Ty;
-template <> struct Ty<kBF16> {
-  static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ unsigned pack2(float x, float y) {
-    bf16x2_t v = {(__bf16)x, (__bf16)y};
-    return bitcast<unsigned>(v);
-  }
-  static __device__ __forceinline__ unsigned short one(float x) { return bitcast<unsigned short>((__bf16)x); }
-};
-template <> struct Ty<kFP16> {
-  static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<f16x8_t>(a), bitcast<f16x8_t>(b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ unsigned pack2(float x, float y) {
-    f16x2_t v = {(_Float16)x, (_Float16)y};
-    return bitcast<unsigned>(v);
-  }
-  static __device__ __forceinline__ unsigned short one(float x) { return bitcast<unsigned short>((_Float16)x); }
-};
-
-// Maximum of a value and its partner lane (lane ^ 32), in every lane.
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // ---------------------------------------------------------------------------
 // LDS tile layouts.  A tile holds BN rows (keys) of D elements; a row is NCH
@@ -373,78 +316,6 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(const FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Split reduction (issue #1248): one work-group per (b, h, row).
-//   LSE = M + ln sum_i exp(LSE_i - M),  M = max_i LSE_i
-//   O   = sum_i exp(LSE_i - LSE) * O_i
-// Splits are summed in increasing order inside each of G lane groups, then the
-// G group sums in increasing group order, so the result is deterministic.
-template <int T_, int D>
-__global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
-  using Tt = Ty<T_>;
-  constexpr int TPS = D / 4;         // threads per split row (float4 each)
-  constexpr int G = 256 / TPS;       // split rows in flight
-  __shared__ float w_s[kMaxSplits];
-  __shared__ float red[256];
-  __shared__ f32x4_t acc_s[G][TPS];
-
-  const int row = blockIdx.x;  // (b*h + head)*s_q + i
-  const int tid = threadIdx.x;
-  const int n = p.n_splits;
-  const int64_t rows = (int64_t)p.b * p.h * p.s_q;
-
-  float mloc = -INFINITY;
-  for (int i = tid; i < n; i += 256) {
-    const float x = p.lse_part[(int64_t)i * rows + row];
-    w_s[i] = x;
-    mloc = fmaxf(mloc, x);
-  }
-  red[tid] = mloc;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  const float Ms = M == -INFINITY ? 0.f : M;
-  float sloc = 0.f;
-  for (int i = tid; i < n; i += 256) sloc += __expf(w_s[i] - Ms);
-  red[tid] = sloc;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
-  }
-  const float tot = red[0];
-  const bool has = M != -INFINITY && tot > 0.f;
-  const float lse = has ? Ms + __logf(tot) : -INFINITY;
-  __syncthreads();
-  for (int i = tid; i < n; i += 256) w_s[i] = has ? __expf(w_s[i] - lse) : 0.f;
-  __syncthreads();
-
-  const int g = tid / TPS, c4 = tid % TPS;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int i = g; i < n; i += G) {
-    const float w = w_s[i];
-    const f32x4_t x = *(const f32x4_t*)(p.o_part + ((int64_t)i * rows + row) * D + c4 * 4);
-    acc += w * x;
-  }
-  acc_s[g][c4] = acc;
-  __syncthreads();
-  if (tid < TPS) {
-    f32x4_t a = acc_s[0][tid];
-    for (int gg = 1; gg < G; ++gg) a += acc_s[gg][tid];
-    const int i = row % p.s_q;
-    const int bh = row / p.s_q;
-    const int bb = bh / p.h, hh = bh % p.h;
-    unsigned short* op = (unsigned short*)p.o + (int64_t)bb * p.os[0] + (int64_t)i * p.os[1] + (int64_t)hh * p.os[2];
-    u32x2_t x = {Tt::pack2(a[0], a[1]), Tt::pack2(a[2], a[3])};
-    *(u32x2_t*)(op + tid * 4) = x;
-    if (tid == 0 && p.lse) p.lse[row] = lse;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Launchers
 
 template <int T_, int D, int NW, int RB, int BN, bool CAUSAL, bool SPLIT>
@@ -459,7 +330,7 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t st) {
 
 template <int T_, int D, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwd_d(const FwdParams& p, hipStream_t st) {
-  if constexpr (D >= 64) return launch_fwd_t<T_, D, 4, 2, 64, CAUSAL, SPLIT>(p, st);
+  if constexpr (D >= 64) return launch_fwd_t<T_, D, 4, kPrefillRB, 64, CAUSAL, SPLIT>(p, st);
   else return launch_fwd_t<T_, D, 4, 1, 32, CAUSAL, SPLIT>(p, st);
 }
 
@@ -479,27 +350,9 @@ static hipError_t launch_fwd_dt(const FwdParams& p, bool causal, bool split, hip
   return split ? launch_fwd_c<T_, false, true>(p, st) : launch_fwd_c<T_, false, false>(p, st);
 }
 
-hipError_t launch_fwd(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st) {
+hipError_t launch_prefill(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st) {
   return dtype == kBF16 ? launch_fwd_dt<kBF16>(p, causal, split, st)
                         : launch_fwd_dt<kFP16>(p, causal, split, st);
-}
-
-int fwd_rows_per_block(int d) { return d >= 64 ? 4 * 2 * 32 : 4 * 1 * 32; }
-
-template <int T_>
-static hipError_t launch_combine_t(const CombineParams& p, hipStream_t st) {
-  const int64_t grid = (int64_t)p.b * p.h * p.s_q;
-  switch (p.d) {
-    case 16: hipLaunchKernelGGL((combine_kernel<T_, 16>), dim3((unsigned)grid), dim3(256), 0, st, p); break;
-    case 32: hipLaunchKernelGGL((combine_kernel<T_, 32>), dim3((unsigned)grid), dim3(256), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((combine_kernel<T_, 64>), dim3((unsigned)grid), dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL((combine_kernel<T_, 128>), dim3((unsigned)grid), dim3(256), 0, st, p); break;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t st) {
-  return dtype == kBF16 ? launch_combine_t<kBF16>(p, st) : launch_combine_t<kFP16>(p, st);
 }
 
 }  // namespace attn

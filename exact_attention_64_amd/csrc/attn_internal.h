@@ -40,10 +40,36 @@ struct CombineParams {
   int n_splits;
 };
 
-// Query rows covered by one work-group of the fused kernel for head dim d.
-int fwd_rows_per_block(int d);
+// Compile-time tunables (overridable with -D for sweeps).
+#ifndef ATTN_PREFILL_RB
+#define ATTN_PREFILL_RB 2   // 32-row blocks per wave in the d >= 64 prefill kernel
+#endif
+#ifndef ATTN_DECODE_WAVES
+#define ATTN_DECODE_WAVES 4 // waves per work-group of the decode kernel
+#endif
+#ifndef ATTN_DECODE_BATCH
+#define ATTN_DECODE_BATCH 8 // wave loads per tensor per batch in the decode kernel
+#endif
+constexpr int kPrefillRB = ATTN_PREFILL_RB;
+constexpr int kDecodeWaves = ATTN_DECODE_WAVES;
+constexpr int kDecodeBatch = ATTN_DECODE_BATCH;
 
-hipError_t launch_fwd(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st);
+// Query rows covered by one work-group for head dim d and s_q query rows: the
+// decode kernel (s_q == 1) takes one row; the prefill kernel 4 waves x RB x 32
+// rows (d >= 64) or 4 x 32 rows (d <= 32).
+inline int fwd_rows_per_block(int d, int s_q) {
+  return s_q == 1 ? 1 : (d >= 64 ? 4 * kPrefillRB * 32 : 4 * 32);
+}
+
+// Fused / split-KV prefill kernel (s_q >= 1; used for s_q > 1).
+hipError_t launch_prefill(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st);
+// One-row decode kernel (s_q == 1).
+hipError_t launch_decode(const FwdParams& p, int dtype, bool split, hipStream_t st);
+// One of the two above, by s_q.  With one query row the bottom-right causal mask
+// hides nothing, so the causal flag does not matter there.
+inline hipError_t launch_fwd(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st) {
+  return p.s_q == 1 ? launch_decode(p, dtype, split, st) : launch_prefill(p, dtype, causal, split, st);
+}
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t st);
 
 }  // namespace attn

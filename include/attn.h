@@ -109,9 +109,10 @@ typedef struct {
 attn_status attn_fwd(const attn_args *args, void *stream);
 
 /* Split count for flash-decoding on `device` (issue #1248): 1 when
- * b*h*ceil(s_q/rows_per_block) already covers the compute units, otherwise
- * enough splits to give each compute unit about two work-groups, capped by
- * ceil(s_k/256) and ATTN_MAX_SPLITS.  Writes the count to *n_out. */
+ * b*h*ceil(s_q/rows_per_block) already covers the compute units (rows_per_block
+ * is 1 for a single query row, else the prefill kernel's row block), otherwise
+ * enough splits to give each compute unit about one work-group, capped by
+ * ceil(s_k/64) and ATTN_MAX_SPLITS.  Writes the count to *n_out. */
 attn_status attn_num_splits(int64_t b, int64_t h, int64_t s_q, int64_t s_k, int64_t d,
                             int device, int32_t *n_out);
 
