@@ -41,6 +41,10 @@ template <> struct Ty<kBF16> {
     return bitcast<unsigned>(v);
   }
   static __device__ __forceinline__ unsigned short one(float x) { return bitcast<unsigned short>((__bf16)x); }
+  static __device__ __forceinline__ void unpack2(unsigned w, float& x, float& y) {
+    x = __uint_as_float(w << 16);
+    y = __uint_as_float(w & 0xffff0000u);
+  }
 };
 template <> struct Ty<kFP16> {
   static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
@@ -51,6 +55,11 @@ template <> struct Ty<kFP16> {
     return bitcast<unsigned>(v);
   }
   static __device__ __forceinline__ unsigned short one(float x) { return bitcast<unsigned short>((_Float16)x); }
+  static __device__ __forceinline__ void unpack2(unsigned w, float& x, float& y) {
+    const f16x2_t h = bitcast<f16x2_t>(w);
+    x = (float)h[0];
+    y = (float)h[1];
+  }
 };
 
 // Maximum of a value and its partner lane (lane ^ 32), in every lane.

@@ -44,6 +44,9 @@ struct CombineParams {
 #ifndef ATTN_PREFILL_RB
 #define ATTN_PREFILL_RB 2   // 32-row blocks per wave in the d >= 64 prefill kernel
 #endif
+#ifndef ATTN_PREFILL_BN
+#define ATTN_PREFILL_BN 32  // keys per tile in the d >= 64 pipelined prefill kernel
+#endif
 #ifndef ATTN_DECODE_WAVES
 #define ATTN_DECODE_WAVES 4 // waves per work-group of the decode kernel
 #endif
@@ -51,6 +54,7 @@ struct CombineParams {
 #define ATTN_DECODE_BATCH 8 // wave loads per tensor per batch in the decode kernel
 #endif
 constexpr int kPrefillRB = ATTN_PREFILL_RB;
+constexpr int kPrefillBN = ATTN_PREFILL_BN;
 constexpr int kDecodeWaves = ATTN_DECODE_WAVES;
 constexpr int kDecodeBatch = ATTN_DECODE_BATCH;
 
