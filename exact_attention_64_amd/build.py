@@ -19,8 +19,12 @@ LIB = os.path.join(HERE, "libattn.so")
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_decode.hip", "attn_combine.hip"]
 
 # Packed fp32 VALU instructions are switched off for every HIP translation unit.
+# MFMA accumulators are kept in VGPRs (the prefill kernel's vector ALU works on
+# the score tile the matrix core produces; AGPR-held scores would cost a copy
+# per element).
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wno-unused-command-line-argument"]
 
 

@@ -62,6 +62,9 @@ template <> struct Ty<kFP16> {
   }
 };
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt(n), lgkmcnt(0), expcnt untouched.
+constexpr int vmcnt_lgkm0(int n) { return (n & 0xF) | (((n >> 4) & 0x3) << 14) | (0x7 << 4); }
+
 // Maximum of a value and its partner lane (lane ^ 32), in every lane.
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -71,5 +74,47 @@ __device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+
+// Packed-pair dot products, conversions and pair sums per storage type.
+template <int T_> struct Dot;
+template <> struct Dot<kBF16> {
+  static __device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(a[i]), bitcast<bf16x2_t>(b[i]), acc, false);
+    return acc;
+  }
+  static __device__ __forceinline__ void unpack8(u32x4_t a, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(a[i] << 16);
+      f[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+    }
+  }
+  // acc + x.lo + x.hi for a packed pair
+  static __device__ __forceinline__ float sum2(unsigned x, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(x), bitcast<bf16x2_t>(0x3f803f80u), acc, false);
+  }
+};
+template <> struct Dot<kFP16> {
+  static __device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2(bitcast<f16x2_t>(a[i]), bitcast<f16x2_t>(b[i]), acc, false);
+    return acc;
+  }
+  static __device__ __forceinline__ void unpack8(u32x4_t a, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2_t h = bitcast<f16x2_t>(a[i]);
+      f[2 * i] = (float)h[0];
+      f[2 * i + 1] = (float)h[1];
+    }
+  }
+  // acc + x.lo + x.hi for a packed pair
+  static __device__ __forceinline__ float sum2(unsigned x, float acc) {
+    return __builtin_amdgcn_fdot2(bitcast<f16x2_t>(x), bitcast<f16x2_t>(0x3c003c00u), acc, false);
+  }
+};
 
 }  // namespace attn

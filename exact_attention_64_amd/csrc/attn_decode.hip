@@ -27,39 +27,6 @@ __device__ __forceinline__ float slot_sum(float x) {
   return x;
 }
 
-template <int T_> struct Dot;
-template <> struct Dot<kBF16> {
-  static __device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b, float acc) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(a[i]), bitcast<bf16x2_t>(b[i]), acc, false);
-    return acc;
-  }
-  static __device__ __forceinline__ void unpack8(u32x4_t a, float* f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __uint_as_float(a[i] << 16);
-      f[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
-    }
-  }
-};
-template <> struct Dot<kFP16> {
-  static __device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b, float acc) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_fdot2(bitcast<f16x2_t>(a[i]), bitcast<f16x2_t>(b[i]), acc, false);
-    return acc;
-  }
-  static __device__ __forceinline__ void unpack8(u32x4_t a, float* f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f16x2_t h = bitcast<f16x2_t>(a[i]);
-      f[2 * i] = (float)h[0];
-      f[2 * i + 1] = (float)h[1];
-    }
-  }
-};
-
 template <int T_, int D, int NWV, bool SPLIT>
 __global__ __launch_bounds__(NWV * 64) void decode_kernel(const FwdParams p) {
   using Tt = Ty<T_>;

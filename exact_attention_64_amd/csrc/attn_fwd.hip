@@ -319,39 +319,48 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(const FwdParams p) {
 // Software-pipelined fused forward for d in {64, 128} (the long-sequence path).
 //
 // Four waves, each owning 64 query rows (two 32-row MFMA blocks, so every K/V
-// fragment read from LDS feeds two MFMAs).  One wave per SIMD: the matrix core
-// and the vector ALU are kept busy by the same wave, so iteration t issues three
-// independent streams of work that the scheduler can interleave:
-//   MFMA  S_{t+1} = K_{t+1} Q^T          (scores of the next tile)
-//   VALU  P_t = exp2(S_t * c - m)        (softmax of the current tile)
-//   MFMA  O  += V_{t-1}^T P_{t-1}^T      (output of the previous tile)
-// K_{t+2} and V_t stream global -> LDS with direct-to-LDS loads while this runs
-// (two buffers each; one barrier per tile).
+// fragment read from LDS feeds two MFMAs), one wave per SIMD.  A tile step:
+//   1. K_{t+2} and V_t stream global -> LDS (direct-to-LDS loads, two buffers
+//      per tensor, one barrier per step);
+//   2. every MFMA operand the step needs is read LDS -> registers at once: the
+//      K_{t+1} fragments and the transposed V_{t-1} fragments (ds_read_b64_tr);
+//   3. one straight-line block issues the 32 MFMAs of
+//        S_{t+1} = K_{t+1} Q^T   and   O += V_{t-1}^T P_{t-1}^T
+//      interleaved with the softmax of tile t on the vector ALU,
+//        P_t = exp2(S_t * c - m),
+//      so the matrix core and the vector ALU of the wave overlap, and no MFMA
+//      waits on an LDS read issued right before it.
+// Q stays in registers for the whole key loop.
 //
-// The output is rescaled lazily: the reference maximum m of a row only moves when
-// a tile's maximum exceeds it by more than TAU (log2 units), so P stays below
-// 2^TAU and O/l are rescaled on a handful of tiles instead of every tile.  O and l
-// always share the same reference, so O/l is the same exact softmax (only the
-// rounding differs), as the online-softmax argument of Lab Notes 07 section 3.3
-// requires.  When the reference moves it moves to the row maximum itself, so a
-// row whose largest score sits in its first visible tile gets weight exactly 1 on
-// that key.
-template <int T_, int D, int BN, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(256, 1) void fwdp_kernel(const FwdParams p) {
+// Softmax bookkeeping per row: a reference m, the sum l of exp2(s*c - m) and O
+// accumulated against the same m, so O/l is the exact softmax (Lab Notes 07,
+// section 3.3: rescaling by the running maximum keeps the result exact).  The
+// common step computes P against the current m without taking a maximum at all;
+// only when a row has no reference yet, or a partial row sum exceeds 2^64 (a
+// score more than 64 above m: P would lose range), does a rare step take the
+// tile's row maxima, move m up to them, multiply O and l by 2^(m_old - m_new)
+// and recompute the tile.  So m never falls below the running maximum by more
+// than 64 and no exponent overflows; rows whose scores fall far below m only
+// lose terms that are negligible against the row's maximum.
+template <int T_, int D, int BN, int RB, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1, RB == 1 ? 2 : 1)))
+void fwdp_kernel(const FwdParams p) {
   using Tt = Ty<T_>;
-  constexpr int NW = 4, RB = 2;
+  constexpr int NW = 4;
   constexpr int NCH = D / 8, KK = D / 16, NB = BN / 32, CB = D / 32, BM = NW * RB * 32;
   constexpr int NT16 = BN / 16;
   constexpr int TILE = BN * D * 2;
   constexpr int WLOADS = TILE / (1024 * NW);  // 1 KB wave loads per tensor per wave
   static_assert(WLOADS >= 1 && TILE % (1024 * NW) == 0, "a tile must split into 1 KB wave loads");
-  constexpr float TAU = 8.f;
+  constexpr float PMAX = 0x1p64f;             // bound on a partial row sum of P
 
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
-  char* const kbuf0 = smem;
-  char* const kbuf1 = smem + TILE;
-  char* const vbuf0 = smem + 2 * TILE;
-  char* const vbuf1 = smem + 3 * TILE;
+  // Four separate LDS objects (not one carved array), so the compiler can tell
+  // that reads of one buffer do not alias loads still landing in another and
+  // need not wait for them.
+  __shared__ __attribute__((aligned(1024))) char kbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -382,8 +391,11 @@ __global__ __launch_bounds__(256, 1) void fwdp_kernel(const FwdParams p) {
   const unsigned short* __restrict__ Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hh * p.ks[2];
   const unsigned short* __restrict__ Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hh * p.vs[2];
   const int64_t ksr = p.ks[1], vsr = p.vs[1];
-
   const int qw0 = q0 + wave * RB * 32;
+
+  // Q fragments (B operand of S^T = K Q^T): row qw0 + rb*32 + l32, d = hi*8 + 16*kk.
+  // Rows past s_q are zero; a negative scale is folded in by negating Q, a zero
+  // scale by zeroing it.
   u32x4_t qf[RB][KK];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -412,67 +424,94 @@ __global__ __launch_bounds__(256, 1) void fwdp_kernel(const FwdParams p) {
   }
   const float c = p.scale_log2;
 
-  // global -> LDS, 16 bytes per lane; slot (row, physical chunk) receives the
-  // logical chunk that the swizzle maps there.  Rows past the range end re-read
-  // the last valid key (finite data; those scores are masked).
-  auto stage = [&](const unsigned short* __restrict__ G, int64_t gs, int tile, char* buf, bool isv) {
+  // ---- global -> LDS staging, 16 bytes per lane.  Slot (row, physical chunk)
+  // receives the logical chunk the swizzle maps there.  Per-lane row offsets are
+  // computed once; a tile adds its key offset.  Rows past the range end (only in
+  // the last tile) re-read the last valid key: finite data, masked scores.
+  int64_t koff[WLOADS], voff[WLOADS];
+#pragma unroll
+  for (int i = 0; i < WLOADS; ++i) {
+    const int slot = (wave * WLOADS + i) * 64 + lane;
+    const int row = slot / NCH, pc = slot % NCH;
+    koff[i] = (int64_t)row * ksr + (pc ^ Swz<D>::k(row)) * 8;
+    voff[i] = (int64_t)row * vsr + (pc ^ Swz<D>::v(row)) * 8;
+  }
+  auto stage = [&](const unsigned short* __restrict__ G, int64_t gs, const int64_t (&goff)[WLOADS],
+                   bool isv, int tile, char* buf) {
     const int k0 = k_lo + tile * BN;
+    if (k0 + BN <= k_hi) {
+      const unsigned short* __restrict__ Gt = G + (int64_t)k0 * gs;
 #pragma unroll
-    for (int i = 0; i < WLOADS; ++i) {
-      const int blk = wave * WLOADS + i;
-      const int slot = blk * 64 + lane;
-      const int row = slot / NCH, pc = slot % NCH;
-      const int ch = pc ^ (isv ? Swz<D>::v(row) : Swz<D>::k(row));
-      const int key = min(k0 + row, k_hi - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(G + (int64_t)key * gs + ch * 8),
-                                       (LDS_AS void*)(buf + blk * 1024), 16, 0, 0);
-    }
-  };
-
-  // S^T (+)= K Q^T over the d-steps [kk0, kk1); kk0 == 0 starts from zero.
-  auto qk = [&](const char* kb, f32x16_t (&s)[NB][RB], int kk0, int kk1) {
-    if (kk0 == 0) {
+      for (int i = 0; i < WLOADS; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(Gt + goff[i]),
+                                         (LDS_AS void*)(buf + (wave * WLOADS + i) * 1024), 16, 0, 0);
+    } else {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[nb][rb][r] = 0.f;
-    }
-#pragma unroll
-    for (int kk = kk0; kk < kk1; ++kk) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int row = nb * 32 + l32;
-        const int ch = hi + 2 * kk;
-        const u32x4_t kf = *(const u32x4_t*)(kb + row * D * 2 + 16 * (ch ^ Swz<D>::k(row)));
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[nb][rb] = Tt::mfma(kf, qf[rb][kk], s[nb][rb]);
+      for (int i = 0; i < WLOADS; ++i) {
+        const int slot = (wave * WLOADS + i) * 64 + lane;
+        const int row = slot / NCH, pc = slot % NCH;
+        const int key = min(k0 + row, k_hi - 1);
+        const int ch = pc ^ (isv ? Swz<D>::v(row) : Swz<D>::k(row));
+        __builtin_amdgcn_global_load_lds((const void*)(G + (int64_t)key * gs + ch * 8),
+                                         (LDS_AS void*)(buf + (wave * WLOADS + i) * 1024), 16, 0, 0);
       }
     }
   };
 
+  // LDS -> registers: K fragments (A operand of S^T = K Q^T) of one tile, and
+  // V^T fragments (A operand of O^T += V^T P^T): d row cb*32 + l32, keys
+  // 16*t16 + 4*hi + {0..3} and 16*t16 + 8 + 4*hi + {0..3}, each half from one
+  // transposed read in which lane x of a 16-lane group fetches 4 columns of key
+  // row x / 4.
   const int g16 = (lane >> 4) & 1, xr = (lane & 15) >> 2, xq = lane & 3;
-  auto pv = [&](const char* vb, const u32x4_t (&pf)[RB][NT16]) {
+  auto read_k = [&](const char* kb, u32x4_t (&kf)[KK][NB]) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int row = nb * 32 + l32;
+        const int ch = hi + 2 * kk;
+        kf[kk][nb] = *(const u32x4_t*)(kb + row * D * 2 + 16 * (ch ^ Swz<D>::k(row)));
+      }
+  };
+  auto read_v = [&](const char* vb, u32x4_t (&vf)[CB][NT16]) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int col = cb * 32 + g16 * 16 + xq * 4;
       const int ch = col / 8, half = (col % 8) / 4;
 #pragma unroll
-      for (int t16 = 0; t16 < NT16; ++t16) {
-        u32x4_t vf;
+      for (int t16 = 0; t16 < NT16; ++t16)
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd) {
           const int row = 16 * t16 + 8 * rd + 4 * hi + xr;
           const char* a = vb + row * D * 2 + 16 * (ch ^ Swz<D>::v(row)) + 8 * half;
           const u32x2_t yy = bitcast<u32x2_t>(__builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(a)));
-          vf[2 * rd] = yy[0];
-          vf[2 * rd + 1] = yy[1];
+          vf[cb][t16][2 * rd] = yy[0];
+          vf[cb][t16][2 * rd + 1] = yy[1];
         }
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[cb][rb] = Tt::mfma(vf, pf[rb][t16], o[cb][rb]);
-      }
     }
+  };
+  auto qk = [&](const u32x4_t (&kf)[KK][NB], f32x16_t (&s)[NB][RB]) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[nb][rb][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[nb][rb] = Tt::mfma(kf[kk][nb], qf[rb][kk], s[nb][rb]);
+  };
+  auto pv = [&](const u32x4_t (&vf)[CB][NT16], const u32x4_t (&pf)[RB][NT16]) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int t16 = 0; t16 < NT16; ++t16)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[cb][rb] = Tt::mfma(vf[cb][t16], pf[rb][t16], o[cb][rb]);
   };
 
   // -inf for keys past the range end and (causal) keys after a row's diagonal.
@@ -490,39 +529,8 @@ __global__ __launch_bounds__(256, 1) void fwdp_kernel(const FwdParams p) {
     }
   };
 
-  // Move the reference maximum of every row of the wave to max(m, tile max) and
-  // multiply O and l by alpha = 2^(m_old - m_new).  A P tile computed with the
-  // old reference and not yet multiplied into O is multiplied by alpha as well
-  // (one extra rounding to fp16/bf16 of that tile, on the few tiles where the
-  // reference moves).
-  auto new_ref = [&](const float (&mt)[RB], float (&alpha)[RB]) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float m_new = fmaxf(m[rb], mt[rb]);
-      alpha[rb] = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rb] - m_new);
-      m[rb] = m_new;
-      l[rb] *= alpha[rb];
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[cb][rb][r] *= alpha[rb];
-    }
-  };
-  auto scale_p = [&](u32x4_t (&pf)[RB][NT16], const float (&alpha)[RB]) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int t16 = 0; t16 < NT16; ++t16)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const unsigned w = pf[rb][t16][e];
-          float a, b;
-          Tt::unpack2(w, a, b);
-          pf[rb][t16][e] = Tt::pack2(a * alpha[rb], b * alpha[rb]);
-        }
-  };
-
-  auto expo = [&](const f32x16_t (&s)[NB][RB], u32x4_t (&pf)[RB][NT16]) {
+  // P = exp2(S * c - m) rounded to the input type; returns this lane's row sums.
+  auto expo = [&](const f32x16_t (&s)[NB][RB], u32x4_t (&pf)[RB][NT16], float (&ls)[RB]) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float m_use = m[rb] == -INFINITY ? 0.f : m[rb];
@@ -535,61 +543,87 @@ __global__ __launch_bounds__(256, 1) void fwdp_kernel(const FwdParams p) {
           const int r0 = 8 * (t16 % 2) + 2 * e;
           const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t16 / 2][rb][r0], c, -m_use));
           const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t16 / 2][rb][r0 + 1], c, -m_use));
-          lsum += a + b;
           x[e] = Tt::pack2(a, b);
+          lsum += a + b;
         }
         pf[rb][t16] = x;
       }
-      l[rb] += lsum;
+      ls[rb] = lsum;
     }
   };
 
-  f32x16_t sA[NB][RB], sB[NB][RB];
-  u32x4_t pA[RB][NT16], pB[RB][NT16];
-
-  if (T > 0) {
-    stage(Kg, ksr, 0, kbuf0, false);
-    if (T > 1) stage(Kg, ksr, 1, kbuf1, false);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    qk(kbuf0, sA, 0, KK);
-  }
-
-  // One tile step, the same straight-line code for every tile: tiles a wave's rows
-  // cannot see are masked rather than skipped (the wave would only wait at the
-  // barrier otherwise), so apart from the mask on diagonal / range-end tiles and
-  // the rare reference move there is no branch, and the MFMA streams (second half
-  // of S_{t+1}, O += P_{t-1} V_{t-1}) interleave with the softmax VALU work.
-  auto iter = [&](int t, bool first, f32x16_t (&s_cur)[NB][RB], f32x16_t (&s_nxt)[NB][RB],
-                  u32x4_t (&p_prev)[RB][NT16], u32x4_t (&p_cur)[RB][NT16],
-                  char* kb_free, const char* kb_next, char* vb_free, const char* vb_prev) {
-    if (t + 2 < T) stage(Kg, ksr, t + 2, kb_free, false);
-    stage(Vg, vsr, t, vb_free, true);
-    const int k0 = k_lo + t * BN;
-    if ((k0 + BN > k_hi) || (CAUSAL && k0 + BN - 1 > qw0 + off)) mask_tile(s_cur, k0);
-    qk(kb_next, s_nxt, 0, KK / 2);
-    float mt[RB];
-    bool need = false;
+  // Rare step: move each row's reference to max(m, tile max), rescale O and l,
+  // and recompute this tile's P against the new reference.
+  auto rebase = [&](const f32x16_t (&s)[NB][RB], u32x4_t (&pf)[RB][NT16], float (&ls)[RB]) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[nb][rb][r]);
-      mt[rb] = pair_max(mx) * c;
-      need |= mt[rb] > m[rb] + TAU;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][rb][r]);
+      const float m_new = fmaxf(m[rb], pair_max(mx) * c);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rb] - m_new);
+      m[rb] = m_new;
+      l[rb] *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[cb][rb][r] *= alpha;
     }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      float alpha[RB];
-      new_ref(mt, alpha);
-      if (!first) scale_p(p_prev, alpha);
-    }
-    qk(kb_next, s_nxt, KK / 2, KK);
-    expo(s_cur, p_cur);
-    if (!first) pv(vb_prev, p_prev);
+    expo(s, pf, ls);
+  };
+
+  f32x16_t sA[NB][RB], sB[NB][RB];
+  u32x4_t pA[RB][NT16], pB[RB][NT16];
+
+  if (T > 0) {
+    stage(Kg, ksr, koff, false, 0, kbuf0);
+    if (T > 1) stage(Kg, ksr, koff, false, 1, kbuf1);
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if (T > 0) {
+    u32x4_t kf[KK][NB];
+    read_k(kbuf0, kf);
+    qk(kf, sA);
+  }
+  // The first step loads K_2 over K_0: every wave must have read K_0 first.
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // Step t: K_t was consumed by the previous step; K_{t+1} sits in kb_next and
+  // V_{t-1} in vb_prev; this step loads K_{t+2} over K_t and V_t over V_{t-2}.
+  auto iter = [&](int t, bool first, f32x16_t (&s)[NB][RB], f32x16_t (&s_next)[NB][RB],
+                  u32x4_t (&p_prev)[RB][NT16], u32x4_t (&p_cur)[RB][NT16],
+                  char* kb_free, const char* kb_next, char* vb_free, const char* vb_prev) {
+    if (t + 2 < T) stage(Kg, ksr, koff, false, t + 2, kb_free);
+    stage(Vg, vsr, voff, true, t, vb_free);
+    const bool has_next = t + 1 < T;
+    u32x4_t kf[KK][NB], vf[CB][NT16];
+    if (has_next) read_k(kb_next, kf);
+    const int k0 = k_lo + t * BN;
+    if ((k0 + BN > k_hi) || (CAUSAL && k0 + BN - 1 > qw0 + off)) mask_tile(s, k0);
+    __builtin_amdgcn_sched_barrier(0);
+    float ls[RB];
+    if (has_next) qk(kf, s_next);
+    expo(s, p_cur, ls);
+    if (!first) { read_v(vb_prev, vf); pv(vf, p_prev); }
+    __builtin_amdgcn_sched_barrier(0);
+    bool bad = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) bad |= m[rb] == -INFINITY || !(ls[rb] <= PMAX);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) rebase(s, p_cur, ls);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l[rb] += ls[rb];
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   if (T > 0) iter(0, true, sA, sB, pB, pA, kbuf0, kbuf1, vbuf0, vbuf1);
@@ -600,8 +634,10 @@ __global__ __launch_bounds__(256, 1) void fwdp_kernel(const FwdParams p) {
   }
   if (t < T) iter(t, false, sB, sA, pA, pB, kbuf1, kbuf0, vbuf1, vbuf0);
   if (T >= 1) {
-    if ((T - 1) & 1) pv(vbuf1, pB);
-    else pv(vbuf0, pA);
+    u32x4_t vf[CB][NT16];
+    read_v((T - 1) & 1 ? vbuf1 : vbuf0, vf);
+    if ((T - 1) & 1) pv(vf, pB);
+    else pv(vf, pA);
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
@@ -656,19 +692,19 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int T_, int D, int BN, bool CAUSAL, bool SPLIT>
+template <int T_, int D, int BN, int RB, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwdp_t(const FwdParams& p, hipStream_t st) {
-  constexpr int BM = 4 * 2 * 32;
+  constexpr int BM = 4 * RB * 32;
   FwdParams q = p;
   q.n_qt = (p.s_q + BM - 1) / BM;
   const int64_t grid = (int64_t)q.n_qt * p.b * p.h * p.n_splits;
-  hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(256), 0, st, q);
+  hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, RB, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(256), 0, st, q);
   return hipGetLastError();
 }
 
 template <int T_, int D, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwd_d(const FwdParams& p, hipStream_t st) {
-  if constexpr (D >= 64) return launch_fwdp_t<T_, D, kPrefillBN, CAUSAL, SPLIT>(p, st);
+  if constexpr (D >= 64) return launch_fwdp_t<T_, D, kPrefillBN, kPrefillRB, CAUSAL, SPLIT>(p, st);
   else return launch_fwd_t<T_, D, 4, 1, 32, CAUSAL, SPLIT>(p, st);
 }
 

@@ -42,10 +42,13 @@ struct CombineParams {
 
 // Compile-time tunables (overridable with -D for sweeps).
 #ifndef ATTN_PREFILL_RB
-#define ATTN_PREFILL_RB 2   // 32-row blocks per wave in the d >= 64 prefill kernel
+#define ATTN_PREFILL_RB 1   // 32-row blocks per wave in the d >= 64 prefill kernel (1: two waves per SIMD)
 #endif
 #ifndef ATTN_PREFILL_BN
 #define ATTN_PREFILL_BN 32  // keys per tile in the d >= 64 pipelined prefill kernel
+#endif
+#ifndef ATTN_PREFILL_NBUF
+#define ATTN_PREFILL_NBUF 2 // LDS buffers per tensor in the pipelined prefill kernel
 #endif
 #ifndef ATTN_DECODE_WAVES
 #define ATTN_DECODE_WAVES 4 // waves per work-group of the decode kernel
@@ -55,6 +58,7 @@ struct CombineParams {
 #endif
 constexpr int kPrefillRB = ATTN_PREFILL_RB;
 constexpr int kPrefillBN = ATTN_PREFILL_BN;
+constexpr int kPrefillNBUF = ATTN_PREFILL_NBUF;
 constexpr int kDecodeWaves = ATTN_DECODE_WAVES;
 constexpr int kDecodeBatch = ATTN_DECODE_BATCH;
 

@@ -282,6 +282,20 @@ def test_deterministic_bitwise():
     assert torch.equal(Op1, Op2) and torch.equal(Lp1, Lp2)
 
 
+def test_deterministic_bitwise_many_blocks():
+    # Many work-groups per compute unit and repeated launches: a missing barrier
+    # between LDS reads and the loads that overwrite the buffer shows up as runs
+    # that differ.
+    say("attn_fwd determinism, causal b=1 s=8192 h=32 d=128 bf16, 6 runs")
+    q, k, v = workloads.make_qkv(1, 8192, 8192, 32, 128, "bf16", seed=5)
+    qd, kd, vd = upload(q, k, v)
+    O1, L1 = ea.attn_fwd(qd, kd, vd, causal=True)
+    for _ in range(5):
+        O2, L2 = ea.attn_fwd(qd, kd, vd, causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
 def test_bad_head_dim_rejected():
     say("attn_fwd bad head dim on device tensors")
     q = torch.zeros((1, 8, 2, 48), dtype=torch.bfloat16, device=DEV)
