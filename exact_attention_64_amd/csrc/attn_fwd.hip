@@ -318,18 +318,18 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(const FwdParams p) {
 // ---------------------------------------------------------------------------
 // Software-pipelined fused forward for d in {64, 128} (the long-sequence path).
 //
-// Four waves, each owning 64 query rows (two 32-row MFMA blocks, so every K/V
-// fragment read from LDS feeds two MFMAs), one wave per SIMD.  A tile step:
-//   1. K_{t+2} and V_t stream global -> LDS (direct-to-LDS loads, two buffers
-//      per tensor, one barrier per step);
-//   2. every MFMA operand the step needs is read LDS -> registers at once: the
-//      K_{t+1} fragments and the transposed V_{t-1} fragments (ds_read_b64_tr);
-//   3. one straight-line block issues the 32 MFMAs of
-//        S_{t+1} = K_{t+1} Q^T   and   O += V_{t-1}^T P_{t-1}^T
-//      interleaved with the softmax of tile t on the vector ALU,
-//        P_t = exp2(S_t * c - m),
-//      so the matrix core and the vector ALU of the wave overlap, and no MFMA
-//      waits on an LDS read issued right before it.
+// NW waves share each K/V tile; every wave owns 32 query rows, so a wave needs
+// at most 256 registers and two waves share each SIMD, one hiding the other's
+// LDS and load latency.  The K and V tiles stream global -> LDS with
+// direct-to-LDS loads through a ring of NBUF buffers per tensor, NBUF - 1 tiles
+// ahead of their use, so a step waits only for loads issued NBUF - 1 steps
+// earlier.  Step t:
+//   1. issues the loads of K_{t+NBUF} and V_{t+NBUF-2};
+//   2. reads the transposed V_{t-1} fragments (ds_read_b64_tr_b16) and issues
+//      O += V_{t-1}^T P_{t-1}^T on the matrix core;
+//   3. reads the K_{t+1} fragments and issues S_{t+1} = K_{t+1} Q^T, while the
+//      vector ALU turns S_t into P_t = exp2(S_t * c - m);
+//   4. waits for K_{t+2} and V_t, and passes one barrier.
 // Q stays in registers for the whole key loop.
 //
 // Softmax bookkeeping per row: a reference m, the sum l of exp2(s*c - m) and O
@@ -342,25 +342,29 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(const FwdParams p) {
 // and recompute the tile.  So m never falls below the running maximum by more
 // than 64 and no exponent overflows; rows whose scores fall far below m only
 // lose terms that are negligible against the row's maximum.
-template <int T_, int D, int BN, int RB, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1, RB == 1 ? 2 : 1)))
+template <int N> struct IC { static constexpr int value = N; };
+
+template <int T_, int D, int BN, int NW, int NBUF, bool PP, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwdp_kernel(const FwdParams p) {
   using Tt = Ty<T_>;
-  constexpr int NW = 4;
-  constexpr int NCH = D / 8, KK = D / 16, NB = BN / 32, CB = D / 32, BM = NW * RB * 32;
+  constexpr int RB = 1, NB = 1;
+  static_assert(BN == 32, "one 32-key MFMA block per tile");
+  constexpr int NCH = D / 8, KK = D / 16, CB = D / 32, BM = NW * 32;
   constexpr int NT16 = BN / 16;
   constexpr int TILE = BN * D * 2;
-  constexpr int WLOADS = TILE / (1024 * NW);  // 1 KB wave loads per tensor per wave
-  static_assert(WLOADS >= 1 && TILE % (1024 * NW) == 0, "a tile must split into 1 KB wave loads");
-  constexpr float PMAX = 0x1p64f;             // bound on a partial row sum of P
+  constexpr int NLOAD = TILE / 1024;            // 1 KB wave loads per tensor per tile
+  constexpr int NLW = NLOAD < NW ? NLOAD : NW;  // waves that take part in the loads
+  constexpr int WL = NLOAD / NLW;               // loads per taking-part wave
+  static_assert(NLOAD >= 1 && NLOAD % NLW == 0, "a tile must split into 1 KB wave loads");
+  static_assert(NBUF == 2 || NBUF == 4, "the step loop is unrolled by NBUF");
+  static_assert(!PP || NW == 8, "ping-pong pairs wave w with wave w + 4 on one SIMD");
+  constexpr int P = NBUF - 1;                   // prefetch distance in tiles
+  constexpr int PAIR = 2 * WL;                  // loads of one (K, V) pair per wave
+  constexpr float PMAX = 0x1p64f;               // bound on a partial row sum of P
 
-  // Four separate LDS objects (not one carved array), so the compiler can tell
-  // that reads of one buffer do not alias loads still landing in another and
-  // need not wait for them.
-  __shared__ __attribute__((aligned(1024))) char kbuf0[TILE];
-  __shared__ __attribute__((aligned(1024))) char kbuf1[TILE];
-  __shared__ __attribute__((aligned(1024))) char vbuf0[TILE];
-  __shared__ __attribute__((aligned(1024))) char vbuf1[TILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf[NBUF][TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf[NBUF][TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -391,15 +395,14 @@ void fwdp_kernel(const FwdParams p) {
   const unsigned short* __restrict__ Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hh * p.ks[2];
   const unsigned short* __restrict__ Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hh * p.vs[2];
   const int64_t ksr = p.ks[1], vsr = p.vs[1];
-  const int qw0 = q0 + wave * RB * 32;
+  const int qw0 = q0 + wave * 32;
 
-  // Q fragments (B operand of S^T = K Q^T): row qw0 + rb*32 + l32, d = hi*8 + 16*kk.
+  // Q fragments (B operand of S^T = K Q^T): row qw0 + l32, d = hi*8 + 16*kk.
   // Rows past s_q are zero; a negative scale is folded in by negating Q, a zero
   // scale by zeroing it.
   u32x4_t qf[RB][KK];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int i = qw0 + rb * 32 + l32;
+  {
+    const int i = qw0 + l32;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4_t x = {0u, 0u, 0u, 0u};
@@ -407,53 +410,53 @@ void fwdp_kernel(const FwdParams p) {
         x = *(const u32x4_t*)(Qg + (int64_t)i * p.qs[1] + hi * 8 + kk * 16);
         if (p.neg_q) x ^= 0x80008000u;
       }
-      qf[rb][kk] = x;
+      qf[0][kk] = x;
     }
   }
 
   f32x16_t o[CB][RB];
   float m[RB], l[RB];
+  m[0] = -INFINITY;
+  l[0] = 0.f;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m[rb] = -INFINITY;
-    l[rb] = 0.f;
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[cb][rb][r] = 0.f;
-  }
+    for (int r = 0; r < 16; ++r) o[cb][0][r] = 0.f;
   const float c = p.scale_log2;
 
-  // ---- global -> LDS staging, 16 bytes per lane.  Slot (row, physical chunk)
-  // receives the logical chunk the swizzle maps there.  Per-lane row offsets are
-  // computed once; a tile adds its key offset.  Rows past the range end (only in
-  // the last tile) re-read the last valid key: finite data, masked scores.
-  int64_t koff[WLOADS], voff[WLOADS];
+  // ---- global -> LDS staging, 16 bytes per lane, by the first NLW waves.
+  // Slot (row, physical chunk) receives the logical chunk the swizzle maps
+  // there.  Per-lane row offsets are computed once; a tile adds its key
+  // offset.  Rows past the range end (only in the last tile) re-read the last
+  // valid key: finite data, masked scores.
+  const bool loader = wave < NLW;
+  int64_t koff[WL], voff[WL];
 #pragma unroll
-  for (int i = 0; i < WLOADS; ++i) {
-    const int slot = (wave * WLOADS + i) * 64 + lane;
-    const int row = slot / NCH, pc = slot % NCH;
+  for (int i = 0; i < WL; ++i) {
+    const int slot = (wave * WL + i) * 64 + lane;
+    const int row = (slot / NCH) % BN, pc = slot % NCH;
     koff[i] = (int64_t)row * ksr + (pc ^ Swz<D>::k(row)) * 8;
     voff[i] = (int64_t)row * vsr + (pc ^ Swz<D>::v(row)) * 8;
   }
-  auto stage = [&](const unsigned short* __restrict__ G, int64_t gs, const int64_t (&goff)[WLOADS],
+  auto stage = [&](const unsigned short* __restrict__ G, int64_t gs, const int64_t (&goff)[WL],
                    bool isv, int tile, char* buf) {
+    if (!loader) return;
     const int k0 = k_lo + tile * BN;
     if (k0 + BN <= k_hi) {
       const unsigned short* __restrict__ Gt = G + (int64_t)k0 * gs;
 #pragma unroll
-      for (int i = 0; i < WLOADS; ++i)
+      for (int i = 0; i < WL; ++i)
         __builtin_amdgcn_global_load_lds((const void*)(Gt + goff[i]),
-                                         (LDS_AS void*)(buf + (wave * WLOADS + i) * 1024), 16, 0, 0);
+                                         (LDS_AS void*)(buf + (wave * WL + i) * 1024), 16, 0, 0);
     } else {
 #pragma unroll
-      for (int i = 0; i < WLOADS; ++i) {
-        const int slot = (wave * WLOADS + i) * 64 + lane;
+      for (int i = 0; i < WL; ++i) {
+        const int slot = (wave * WL + i) * 64 + lane;
         const int row = slot / NCH, pc = slot % NCH;
         const int key = min(k0 + row, k_hi - 1);
         const int ch = pc ^ (isv ? Swz<D>::v(row) : Swz<D>::k(row));
         __builtin_amdgcn_global_load_lds((const void*)(G + (int64_t)key * gs + ch * 8),
-                                         (LDS_AS void*)(buf + (wave * WLOADS + i) * 1024), 16, 0, 0);
+                                         (LDS_AS void*)(buf + (wave * WL + i) * 1024), 16, 0, 0);
       }
     }
   };
@@ -466,13 +469,11 @@ void fwdp_kernel(const FwdParams p) {
   const int g16 = (lane >> 4) & 1, xr = (lane & 15) >> 2, xq = lane & 3;
   auto read_k = [&](const char* kb, u32x4_t (&kf)[KK][NB]) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int row = nb * 32 + l32;
-        const int ch = hi + 2 * kk;
-        kf[kk][nb] = *(const u32x4_t*)(kb + row * D * 2 + 16 * (ch ^ Swz<D>::k(row)));
-      }
+    for (int kk = 0; kk < KK; ++kk) {
+      const int row = l32;
+      const int ch = hi + 2 * kk;
+      kf[kk][0] = *(const u32x4_t*)(kb + row * D * 2 + 16 * (ch ^ Swz<D>::k(row)));
+    }
   };
   auto read_v = [&](const char* vb, u32x4_t (&vf)[CB][NT16]) {
 #pragma unroll
@@ -493,83 +494,73 @@ void fwdp_kernel(const FwdParams p) {
   };
   auto qk = [&](const u32x4_t (&kf)[KK][NB], f32x16_t (&s)[NB][RB]) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int r = 0; r < 16; ++r) s[0][0][r] = 0.f;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[nb][rb][r] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[nb][rb] = Tt::mfma(kf[kk][nb], qf[rb][kk], s[nb][rb]);
+    for (int kk = 0; kk < KK; ++kk) s[0][0] = Tt::mfma(kf[kk][0], qf[0][kk], s[0][0]);
   };
   auto pv = [&](const u32x4_t (&vf)[CB][NT16], const u32x4_t (&pf)[RB][NT16]) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int t16 = 0; t16 < NT16; ++t16)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[cb][rb] = Tt::mfma(vf[cb][t16], pf[rb][t16], o[cb][rb]);
+      for (int t16 = 0; t16 < NT16; ++t16) o[cb][0] = Tt::mfma(vf[cb][t16], pf[0][t16], o[cb][0]);
   };
 
   // -inf for keys past the range end and (causal) keys after a row's diagonal.
   auto mask_tile = [&](f32x16_t (&s)[NB][RB], int k0) {
+    const int i = qw0 + l32;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int i = qw0 + rb * 32 + l32;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + nb * 32 + (r / 4) * 8 + hi * 4 + (r % 4);
-          if (key >= k_hi || (CAUSAL && key > i + off)) s[nb][rb][r] = -INFINITY;
-        }
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + (r / 4) * 8 + hi * 4 + (r % 4);
+      if (key >= k_hi || (CAUSAL && key > i + off)) s[0][0][r] = -INFINITY;
     }
   };
 
-  // P = exp2(S * c - m) rounded to the input type; returns this lane's row sums.
+  // P = exp2(S * c - m) rounded to the input type; returns this lane's row sum.
   auto expo = [&](const f32x16_t (&s)[NB][RB], u32x4_t (&pf)[RB][NT16], float (&ls)[RB]) {
+    const float m_use = m[0] == -INFINITY ? 0.f : m[0];
+    float lsum = 0.f;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float m_use = m[rb] == -INFINITY ? 0.f : m[rb];
-      float lsum = 0.f;
+    for (int t16 = 0; t16 < NT16; ++t16) {
+      u32x4_t x;
 #pragma unroll
-      for (int t16 = 0; t16 < NT16; ++t16) {
-        u32x4_t x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r0 = 8 * (t16 % 2) + 2 * e;
-          const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t16 / 2][rb][r0], c, -m_use));
-          const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t16 / 2][rb][r0 + 1], c, -m_use));
-          x[e] = Tt::pack2(a, b);
-          lsum += a + b;
-        }
-        pf[rb][t16] = x;
+      for (int e = 0; e < 4; ++e) {
+        const int r0 = 8 * t16 + 2 * e;
+        const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][0][r0], c, -m_use));
+        const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][0][r0 + 1], c, -m_use));
+        x[e] = Tt::pack2(a, b);
+        lsum += a + b;
       }
-      ls[rb] = lsum;
+      pf[0][t16] = x;
     }
+    ls[0] = lsum;
   };
 
   // Rare step: move each row's reference to max(m, tile max), rescale O and l,
   // and recompute this tile's P against the new reference.
-  auto rebase = [&](const f32x16_t (&s)[NB][RB], u32x4_t (&pf)[RB][NT16], float (&ls)[RB]) {
+  // With `defer`, O's factor is kept in alpha_p and applied by the next O update
+  // step (once the pending P_{t-1} V_{t-1} product, still relative to the old
+  // reference, has been added).
+  bool pend = false;
+  float alpha_p = 1.f;
+  auto scale_o = [&](float alpha) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float mx = -INFINITY;
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int r = 0; r < 16; ++r) o[cb][0][r] *= alpha;
+  };
+  auto rebase = [&](const f32x16_t (&s)[NB][RB], u32x4_t (&pf)[RB][NT16], float (&ls)[RB], bool defer) {
+    float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][rb][r]);
-      const float m_new = fmaxf(m[rb], pair_max(mx) * c);
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rb] - m_new);
-      m[rb] = m_new;
-      l[rb] *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[cb][rb][r] *= alpha;
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[0][0][r]);
+    const float m_new = fmaxf(m[0], pair_max(mx) * c);
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[0] - m_new);
+    m[0] = m_new;
+    l[0] *= alpha;
+    if (defer) {
+      alpha_p = alpha;
+      pend = true;
+    } else {
+      scale_o(alpha);
     }
     expo(s, pf, ls);
   };
@@ -577,77 +568,162 @@ void fwdp_kernel(const FwdParams p) {
   f32x16_t sA[NB][RB], sB[NB][RB];
   u32x4_t pA[RB][NT16], pB[RB][NT16];
 
+  // Prologue: K_0 and K_1, then the (K_{j+2}, V_j) pairs j < NBUF - 2, so that
+  // step t always finds the pairs up to t + NBUF - 3 issued.  `full`: every
+  // prologue load was issued, so the wait counts below are exact (otherwise
+  // the prologue waits for everything).
+  const bool full = T > P;
   if (T > 0) {
-    stage(Kg, ksr, koff, false, 0, kbuf0);
-    if (T > 1) stage(Kg, ksr, koff, false, 1, kbuf1);
+    stage(Kg, ksr, koff, false, 0, kbuf[0]);
+    if (T > 1) stage(Kg, ksr, koff, false, 1, kbuf[1]);
+#pragma unroll
+    for (int j = 0; j + 2 <= P; ++j) {
+      if (j + 2 < T) stage(Kg, ksr, koff, false, j + 2, kbuf[(j + 2) % NBUF]);
+      if (j < T) stage(Vg, vsr, voff, true, j, vbuf[j % NBUF]);
+    }
   }
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0);
+  if (full) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(WL + (P - 1) * PAIR));
+  else __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   if (T > 0) {
     u32x4_t kf[KK][NB];
-    read_k(kbuf0, kf);
+    read_k(kbuf[0], kf);
     qk(kf, sA);
   }
-  // The first step loads K_2 over K_0: every wave must have read K_0 first.
+  // K_1 has landed, and every wave has read K_0 (step 0 loads over it).
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0);
+  if (full) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0((P - 1) * PAIR));
+  else __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
-  // Step t: K_t was consumed by the previous step; K_{t+1} sits in kb_next and
-  // V_{t-1} in vb_prev; this step loads K_{t+2} over K_t and V_t over V_{t-2}.
-  auto iter = [&](int t, bool first, f32x16_t (&s)[NB][RB], f32x16_t (&s_next)[NB][RB],
+  // Step t.  Buffers: K_t's slot takes K_{t+NBUF}; K_{t+1} is read; V_{t-2}'s
+  // slot takes V_{t+NBUF-2}; V_{t-1} is read.  At the end, the loads of
+  // K_{t+2} and V_t (issued NBUF - 1 steps earlier) must have landed; later
+  // pairs may still be in flight.
+  auto iter = [&](auto GC, int t, bool first, f32x16_t (&s)[NB][RB], f32x16_t (&s_next)[NB][RB],
                   u32x4_t (&p_prev)[RB][NT16], u32x4_t (&p_cur)[RB][NT16],
-                  char* kb_free, const char* kb_next, char* vb_free, const char* vb_prev) {
-    if (t + 2 < T) stage(Kg, ksr, koff, false, t + 2, kb_free);
-    stage(Vg, vsr, voff, true, t, vb_free);
+                  char* kb_w, const char* kb_r, char* vb_w, const char* vb_r) __attribute__((always_inline)) {
+    constexpr int grp = decltype(GC)::value;
+    if (t + P + 1 < T) stage(Kg, ksr, koff, false, t + P + 1, kb_w);
+    if (t + P - 1 < T) stage(Vg, vsr, voff, true, t + P - 1, vb_w);
     const bool has_next = t + 1 < T;
-    u32x4_t kf[KK][NB], vf[CB][NT16];
-    if (has_next) read_k(kb_next, kf);
     const int k0 = k_lo + t * BN;
-    if ((k0 + BN > k_hi) || (CAUSAL && k0 + BN - 1 > qw0 + off)) mask_tile(s, k0);
-    __builtin_amdgcn_sched_barrier(0);
-    float ls[RB];
-    if (has_next) qk(kf, s_next);
-    expo(s, p_cur, ls);
-    if (!first) { read_v(vb_prev, vf); pv(vf, p_prev); }
-    __builtin_amdgcn_sched_barrier(0);
-    bool bad = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) bad |= m[rb] == -INFINITY || !(ls[rb] <= PMAX);
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) rebase(s, p_cur, ls);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) l[rb] += ls[rb];
+    const bool need_mask = (k0 + BN > k_hi) || (CAUSAL && k0 + BN - 1 > qw0 + off);
+    if constexpr (!PP) {
+      // One wave mixes both halves; the other wave on the SIMD fills the gaps.
+      u32x4_t kf[KK][NB], vf[CB][NT16];
+      if (!first) read_v(vb_r, vf);
+      if (need_mask) mask_tile(s, k0);
+      __builtin_amdgcn_sched_barrier(0);
+      float ls[RB];
+      if (!first) pv(vf, p_prev);
+      if (has_next) read_k(kb_r, kf);
+      expo(s, p_cur, ls);
+      if (has_next) qk(kf, s_next);
+      __builtin_amdgcn_sched_barrier(0);
+      const bool bad = m[0] == -INFINITY || !(ls[0] <= PMAX);
+      if (__builtin_amdgcn_ballot_w64(bad) != 0) rebase(s, p_cur, ls, false);
+      l[0] += ls[0];
+    } else {
+      // Ping-pong: waves 0-3 run the matrix-core half while waves 4-7 (their
+      // SIMD partners) run the vector half, then the two swap.
+      auto mhalf = [&]() __attribute__((always_inline)) {
+        if constexpr (kPrefillPrio) __builtin_amdgcn_s_setprio(1);
+        u32x4_t kf[KK][NB], vf[CB][NT16];
+        if (!first) {
+          read_v(vb_r, vf);
+          pv(vf, p_prev);
+        }
+        if (pend) {
+          scale_o(alpha_p);
+          pend = false;
+        }
+        if (has_next) {
+          read_k(kb_r, kf);
+          qk(kf, s_next);
+        }
+        if constexpr (kPrefillPrio) __builtin_amdgcn_s_setprio(0);
+      };
+      auto vhalf = [&](bool defer) __attribute__((always_inline)) {
+        if (need_mask) mask_tile(s, k0);
+        float ls[RB];
+        expo(s, p_cur, ls);
+        const bool bad = m[0] == -INFINITY || !(ls[0] <= PMAX);
+        if (__builtin_amdgcn_ballot_w64(bad) != 0) rebase(s, p_cur, ls, defer);
+        l[0] += ls[0];
+      };
+      if constexpr (grp == 0) {
+        mhalf();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        vhalf(false);
+      } else {
+        vhalf(true);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        mhalf();
+      }
+    }
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0);
+    if (t + P + 1 < T) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0((P - 1) * PAIR));
+    else __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-
-  if (T > 0) iter(0, true, sA, sB, pB, pA, kbuf0, kbuf1, vbuf0, vbuf1);
-  int t = 1;
-  for (; t + 1 < T; t += 2) {
-    iter(t, false, sB, sA, pA, pB, kbuf1, kbuf0, vbuf1, vbuf0);
-    iter(t + 1, false, sA, sB, pB, pA, kbuf0, kbuf1, vbuf0, vbuf1);
+  // One step with r = t % NBUF known at compile time, so every LDS address is
+  // an immediate offset.
+  auto step = [&](auto GC, int t, auto RC) __attribute__((always_inline)) {
+    constexpr int r = decltype(RC)::value;
+    char* kb_w = kbuf[r];
+    const char* kb_r = kbuf[(r + 1) % NBUF];
+    char* vb_w = vbuf[(r + NBUF - 2) % NBUF];
+    const char* vb_r = vbuf[(r + NBUF - 1) % NBUF];
+    if constexpr (r % 2 == 1) iter(GC, t, false, sB, sA, pA, pB, kb_w, kb_r, vb_w, vb_r);
+    else iter(GC, t, false, sA, sB, pB, pA, kb_w, kb_r, vb_w, vb_r);
+  };
+  // The key loop; with ping-pong, each wave group gets its own copy.
+  auto loop = [&](auto GC) __attribute__((always_inline)) {
+    if (T > 0) iter(GC, 0, true, sA, sB, pB, pA, kbuf[0], kbuf[1], vbuf[NBUF - 2], vbuf[NBUF - 1]);
+    int t = 1;
+    for (; t + NBUF <= T; t += NBUF) {
+      step(GC, t, IC<1 % NBUF>{});
+      step(GC, t + 1, IC<2 % NBUF>{});
+      if constexpr (NBUF == 4) {
+        step(GC, t + 2, IC<3>{});
+        step(GC, t + 3, IC<0>{});
+      }
+    }
+    if (t < T) step(GC, t, IC<1 % NBUF>{});
+    if constexpr (NBUF == 4) {
+      if (t + 1 < T) step(GC, t + 1, IC<2>{});
+      if (t + 2 < T) step(GC, t + 2, IC<3>{});
+    }
+  };
+  if constexpr (PP) {
+    if (wave < 4) loop(IC<0>{});
+    else loop(IC<1>{});
+  } else {
+    loop(IC<0>{});
   }
-  if (t < T) iter(t, false, sB, sA, pA, pB, kbuf1, kbuf0, vbuf1, vbuf0);
   if (T >= 1) {
     u32x4_t vf[CB][NT16];
-    read_v((T - 1) & 1 ? vbuf1 : vbuf0, vf);
+    read_v(vbuf[(T - 1) % NBUF], vf);
     if ((T - 1) & 1) pv(vf, pB);
     else pv(vf, pA);
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int i = qw0 + rb * 32 + l32;
-    const float lt = pair_sum(l[rb]);
+  {
+    const int i = qw0 + l32;
+    const float lt = pair_sum(l[0]);
     const bool has = lt > 0.f;
     const float inv = has ? 1.f / lt : 0.f;
-    const float lse = has ? (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    const float lse = has ? (m[0] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
     if (i < p.s_q) {
       if (SPLIT) {
         const int64_t rowi = (((int64_t)split * p.b + bb) * p.h + hh) * p.s_q + i;
@@ -657,8 +733,8 @@ void fwdp_kernel(const FwdParams p) {
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const int col = cb * 32 + r4 * 8 + hi * 4;
-            f32x4_t x = {o[cb][rb][4 * r4] * inv, o[cb][rb][4 * r4 + 1] * inv,
-                         o[cb][rb][4 * r4 + 2] * inv, o[cb][rb][4 * r4 + 3] * inv};
+            f32x4_t x = {o[cb][0][4 * r4] * inv, o[cb][0][4 * r4 + 1] * inv,
+                         o[cb][0][4 * r4 + 2] * inv, o[cb][0][4 * r4 + 3] * inv};
             *(f32x4_t*)(op + col) = x;
           }
         if (hi == 0) p.lse_part[rowi] = lse;
@@ -669,8 +745,8 @@ void fwdp_kernel(const FwdParams p) {
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const int col = cb * 32 + r4 * 8 + hi * 4;
-            u32x2_t x = {Tt::pack2(o[cb][rb][4 * r4] * inv, o[cb][rb][4 * r4 + 1] * inv),
-                         Tt::pack2(o[cb][rb][4 * r4 + 2] * inv, o[cb][rb][4 * r4 + 3] * inv)};
+            u32x2_t x = {Tt::pack2(o[cb][0][4 * r4] * inv, o[cb][0][4 * r4 + 1] * inv),
+                         Tt::pack2(o[cb][0][4 * r4 + 2] * inv, o[cb][0][4 * r4 + 3] * inv)};
             *(u32x2_t*)(op + col) = x;
           }
         if (hi == 0 && p.lse) p.lse[((int64_t)bb * p.h + hh) * p.s_q + i] = lse;
@@ -692,19 +768,20 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int T_, int D, int BN, int RB, bool CAUSAL, bool SPLIT>
+template <int T_, int D, int BN, int NW, int NBUF, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwdp_t(const FwdParams& p, hipStream_t st) {
-  constexpr int BM = 4 * RB * 32;
+  constexpr int BM = NW * 32;
+  constexpr bool PP = NW == 8 && kPrefillPP;
   FwdParams q = p;
   q.n_qt = (p.s_q + BM - 1) / BM;
   const int64_t grid = (int64_t)q.n_qt * p.b * p.h * p.n_splits;
-  hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, RB, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(256), 0, st, q);
+  hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, NW, NBUF, PP, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
   return hipGetLastError();
 }
 
 template <int T_, int D, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwd_d(const FwdParams& p, hipStream_t st) {
-  if constexpr (D >= 64) return launch_fwdp_t<T_, D, kPrefillBN, kPrefillRB, CAUSAL, SPLIT>(p, st);
+  if constexpr (D >= 64) return launch_fwdp_t<T_, D, kPrefillBN, kPrefillNW, kPrefillNBUF, CAUSAL, SPLIT>(p, st);
   else return launch_fwd_t<T_, D, 4, 1, 32, CAUSAL, SPLIT>(p, st);
 }
 

@@ -1,5 +1,5 @@
 // Internal interface between the C-ABI front end (attn_api.cpp) and the gfx950
-// kernels (attn_kernels.hip).  Not installed; the public interface is attn.h.
+// kernels (attn_fwd.hip, attn_decode.hip, attn_combine.hip).  Not installed; the public interface is attn.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -41,14 +41,20 @@ struct CombineParams {
 };
 
 // Compile-time tunables (overridable with -D for sweeps).
-#ifndef ATTN_PREFILL_RB
-#define ATTN_PREFILL_RB 1   // 32-row blocks per wave in the d >= 64 prefill kernel (1: two waves per SIMD)
+#ifndef ATTN_PREFILL_NW
+#define ATTN_PREFILL_NW 4   // waves per work-group of the d >= 64 prefill kernel (32 rows each)
 #endif
 #ifndef ATTN_PREFILL_BN
-#define ATTN_PREFILL_BN 32  // keys per tile in the d >= 64 pipelined prefill kernel
+#define ATTN_PREFILL_BN 32  // keys per tile of the d >= 64 prefill kernel
 #endif
 #ifndef ATTN_PREFILL_NBUF
-#define ATTN_PREFILL_NBUF 2 // LDS buffers per tensor in the pipelined prefill kernel
+#define ATTN_PREFILL_NBUF 4 // LDS ring buffers per tensor (prefetch depth + 1), 2 or 4
+#endif
+#ifndef ATTN_PREFILL_PP
+#define ATTN_PREFILL_PP 1   // with 8 waves: ping-pong the matrix-core and vector halves
+#endif
+#ifndef ATTN_PREFILL_PRIO
+#define ATTN_PREFILL_PRIO 0 // raise the wave priority during the matrix-core half
 #endif
 #ifndef ATTN_DECODE_WAVES
 #define ATTN_DECODE_WAVES 4 // waves per work-group of the decode kernel
@@ -56,17 +62,19 @@ struct CombineParams {
 #ifndef ATTN_DECODE_BATCH
 #define ATTN_DECODE_BATCH 8 // wave loads per tensor per batch in the decode kernel
 #endif
-constexpr int kPrefillRB = ATTN_PREFILL_RB;
+constexpr int kPrefillNW = ATTN_PREFILL_NW;
 constexpr int kPrefillBN = ATTN_PREFILL_BN;
 constexpr int kPrefillNBUF = ATTN_PREFILL_NBUF;
+constexpr bool kPrefillPP = ATTN_PREFILL_PP != 0;
+constexpr bool kPrefillPrio = ATTN_PREFILL_PRIO != 0;
 constexpr int kDecodeWaves = ATTN_DECODE_WAVES;
 constexpr int kDecodeBatch = ATTN_DECODE_BATCH;
 
 // Query rows covered by one work-group for head dim d and s_q query rows: the
-// decode kernel (s_q == 1) takes one row; the prefill kernel 4 waves x RB x 32
-// rows (d >= 64) or 4 x 32 rows (d <= 32).
+// decode kernel (s_q == 1) takes one row; the prefill kernel NW x 32 rows
+// (d >= 64) or 4 x 32 rows (d <= 32).
 inline int fwd_rows_per_block(int d, int s_q) {
-  return s_q == 1 ? 1 : (d >= 64 ? 4 * kPrefillRB * 32 : 4 * 32);
+  return s_q == 1 ? 1 : (d >= 64 ? kPrefillNW * 32 : 4 * 32);
 }
 
 // Fused / split-KV prefill kernel (s_q >= 1; used for s_q > 1).
