@@ -344,7 +344,23 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(const FwdParams p) {
 // lose terms that are negligible against the row's maximum.
 template <int N> struct IC { static constexpr int value = N; };
 
-template <int T_, int D, int BN, int NW, int NBUF, bool PP, bool CAUSAL, bool SPLIT>
+// One direct-to-LDS wave load: lane i copies 16 bytes from gptr to LDS byte
+// address lds + 16 i (lds is wave-uniform).  Written as inline asm so that the
+// compiler does not treat the LDS write as aliasing the reads of other ring
+// slots and wait for every load in flight before them (it cannot bound the
+// per-wave offset); the kernel orders these loads with its own s_waitcnt
+// vmcnt and barriers.  Loads complete in order, so the compiler's own vmcnt
+// waits for other loads stay correct.  The s_nop covers the M0 -> LDS DMA
+// hazard.
+__device__ __forceinline__ void lds_dma16(const void* gptr, const char* lds) {
+  const unsigned m0v = (unsigned)(uintptr_t)(const LDS_AS char*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0v), "v"(gptr)
+               : "memory", "m0");
+}
+
+template <int T_, int D, int BN, int NW, int NBUF, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwdp_kernel(const FwdParams p) {
   using Tt = Ty<T_>;
@@ -358,7 +374,6 @@ void fwdp_kernel(const FwdParams p) {
   constexpr int WL = NLOAD / NLW;               // loads per taking-part wave
   static_assert(NLOAD >= 1 && NLOAD % NLW == 0, "a tile must split into 1 KB wave loads");
   static_assert(NBUF == 2 || NBUF == 4, "the step loop is unrolled by NBUF");
-  static_assert(!PP || NW == 8, "ping-pong pairs wave w with wave w + 4 on one SIMD");
   constexpr int P = NBUF - 1;                   // prefetch distance in tiles
   constexpr int PAIR = 2 * WL;                  // loads of one (K, V) pair per wave
   constexpr float PMAX = 0x1p64f;               // bound on a partial row sum of P
@@ -413,6 +428,9 @@ void fwdp_kernel(const FwdParams p) {
       qf[0][kk] = x;
     }
   }
+  // Wait for Q here, on every path: a load still pending where the key loop
+  // starts would make the compiler wait for all loads (vmcnt(0)) inside it.
+  __builtin_amdgcn_s_waitcnt(0);
 
   f32x16_t o[CB][RB];
   float m[RB], l[RB];
@@ -446,8 +464,7 @@ void fwdp_kernel(const FwdParams p) {
       const unsigned short* __restrict__ Gt = G + (int64_t)k0 * gs;
 #pragma unroll
       for (int i = 0; i < WL; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(Gt + goff[i]),
-                                         (LDS_AS void*)(buf + (wave * WL + i) * 1024), 16, 0, 0);
+        lds_dma16((const void*)(Gt + goff[i]), buf + (wave * WL + i) * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < WL; ++i) {
@@ -455,8 +472,7 @@ void fwdp_kernel(const FwdParams p) {
         const int row = slot / NCH, pc = slot % NCH;
         const int key = min(k0 + row, k_hi - 1);
         const int ch = pc ^ (isv ? Swz<D>::v(row) : Swz<D>::k(row));
-        __builtin_amdgcn_global_load_lds((const void*)(G + (int64_t)key * gs + ch * 8),
-                                         (LDS_AS void*)(buf + (wave * WL + i) * 1024), 16, 0, 0);
+        lds_dma16((const void*)(G + (int64_t)key * gs + ch * 8), buf + (wave * WL + i) * 1024);
       }
     }
   };
@@ -537,18 +553,7 @@ void fwdp_kernel(const FwdParams p) {
 
   // Rare step: move each row's reference to max(m, tile max), rescale O and l,
   // and recompute this tile's P against the new reference.
-  // With `defer`, O's factor is kept in alpha_p and applied by the next O update
-  // step (once the pending P_{t-1} V_{t-1} product, still relative to the old
-  // reference, has been added).
-  bool pend = false;
-  float alpha_p = 1.f;
-  auto scale_o = [&](float alpha) {
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[cb][0][r] *= alpha;
-  };
-  auto rebase = [&](const f32x16_t (&s)[NB][RB], u32x4_t (&pf)[RB][NT16], float (&ls)[RB], bool defer) {
+  auto rebase = [&](const f32x16_t (&s)[NB][RB], u32x4_t (&pf)[RB][NT16], float (&ls)[RB]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[0][0][r]);
@@ -556,12 +561,10 @@ void fwdp_kernel(const FwdParams p) {
     const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[0] - m_new);
     m[0] = m_new;
     l[0] *= alpha;
-    if (defer) {
-      alpha_p = alpha;
-      pend = true;
-    } else {
-      scale_o(alpha);
-    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[cb][0][r] *= alpha;
     expo(s, pf, ls);
   };
 
@@ -603,72 +606,30 @@ void fwdp_kernel(const FwdParams p) {
   // slot takes V_{t+NBUF-2}; V_{t-1} is read.  At the end, the loads of
   // K_{t+2} and V_t (issued NBUF - 1 steps earlier) must have landed; later
   // pairs may still be in flight.
-  auto iter = [&](auto GC, int t, bool first, f32x16_t (&s)[NB][RB], f32x16_t (&s_next)[NB][RB],
+  // HC: 1 when the caller knows that tile t + 1 exists, which keeps the
+  // product/softmax block of the step free of branches (the scheduler cannot
+  // interleave across them).
+  auto iter = [&](auto HC, int t, bool first, f32x16_t (&s)[NB][RB], f32x16_t (&s_next)[NB][RB],
                   u32x4_t (&p_prev)[RB][NT16], u32x4_t (&p_cur)[RB][NT16],
                   char* kb_w, const char* kb_r, char* vb_w, const char* vb_r) __attribute__((always_inline)) {
-    constexpr int grp = decltype(GC)::value;
     if (t + P + 1 < T) stage(Kg, ksr, koff, false, t + P + 1, kb_w);
     if (t + P - 1 < T) stage(Vg, vsr, voff, true, t + P - 1, vb_w);
-    const bool has_next = t + 1 < T;
+    const bool has_next = decltype(HC)::value == 1 || t + 1 < T;
     const int k0 = k_lo + t * BN;
     const bool need_mask = (k0 + BN > k_hi) || (CAUSAL && k0 + BN - 1 > qw0 + off);
-    if constexpr (!PP) {
-      // One wave mixes both halves; the other wave on the SIMD fills the gaps.
-      u32x4_t kf[KK][NB], vf[CB][NT16];
-      if (!first) read_v(vb_r, vf);
-      if (need_mask) mask_tile(s, k0);
-      __builtin_amdgcn_sched_barrier(0);
-      float ls[RB];
-      if (!first) pv(vf, p_prev);
-      if (has_next) read_k(kb_r, kf);
-      expo(s, p_cur, ls);
-      if (has_next) qk(kf, s_next);
-      __builtin_amdgcn_sched_barrier(0);
-      const bool bad = m[0] == -INFINITY || !(ls[0] <= PMAX);
-      if (__builtin_amdgcn_ballot_w64(bad) != 0) rebase(s, p_cur, ls, false);
-      l[0] += ls[0];
-    } else {
-      // Ping-pong: waves 0-3 run the matrix-core half while waves 4-7 (their
-      // SIMD partners) run the vector half, then the two swap.
-      auto mhalf = [&]() __attribute__((always_inline)) {
-        if constexpr (kPrefillPrio) __builtin_amdgcn_s_setprio(1);
-        u32x4_t kf[KK][NB], vf[CB][NT16];
-        if (!first) {
-          read_v(vb_r, vf);
-          pv(vf, p_prev);
-        }
-        if (pend) {
-          scale_o(alpha_p);
-          pend = false;
-        }
-        if (has_next) {
-          read_k(kb_r, kf);
-          qk(kf, s_next);
-        }
-        if constexpr (kPrefillPrio) __builtin_amdgcn_s_setprio(0);
-      };
-      auto vhalf = [&](bool defer) __attribute__((always_inline)) {
-        if (need_mask) mask_tile(s, k0);
-        float ls[RB];
-        expo(s, p_cur, ls);
-        const bool bad = m[0] == -INFINITY || !(ls[0] <= PMAX);
-        if (__builtin_amdgcn_ballot_w64(bad) != 0) rebase(s, p_cur, ls, defer);
-        l[0] += ls[0];
-      };
-      if constexpr (grp == 0) {
-        mhalf();
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        vhalf(false);
-      } else {
-        vhalf(true);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        mhalf();
-      }
-    }
+    u32x4_t kf[KK][NB], vf[CB][NT16];
+    if (!first) read_v(vb_r, vf);
+    if (need_mask) mask_tile(s, k0);
+    __builtin_amdgcn_sched_barrier(0);
+    float ls[RB];
+    if (!first) pv(vf, p_prev);
+    if (has_next) read_k(kb_r, kf);
+    expo(s, p_cur, ls);
+    if (has_next) qk(kf, s_next);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool bad = m[0] == -INFINITY || !(ls[0] <= PMAX);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) rebase(s, p_cur, ls);
+    l[0] += ls[0];
     asm volatile("" ::: "memory");
     if (t + P + 1 < T) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0((P - 1) * PAIR));
     else __builtin_amdgcn_s_waitcnt(0);
@@ -677,38 +638,32 @@ void fwdp_kernel(const FwdParams p) {
   };
   // One step with r = t % NBUF known at compile time, so every LDS address is
   // an immediate offset.
-  auto step = [&](auto GC, int t, auto RC) __attribute__((always_inline)) {
+  auto step = [&](auto HC, int t, auto RC) __attribute__((always_inline)) {
     constexpr int r = decltype(RC)::value;
     char* kb_w = kbuf[r];
     const char* kb_r = kbuf[(r + 1) % NBUF];
     char* vb_w = vbuf[(r + NBUF - 2) % NBUF];
     const char* vb_r = vbuf[(r + NBUF - 1) % NBUF];
-    if constexpr (r % 2 == 1) iter(GC, t, false, sB, sA, pA, pB, kb_w, kb_r, vb_w, vb_r);
-    else iter(GC, t, false, sA, sB, pB, pA, kb_w, kb_r, vb_w, vb_r);
+    if constexpr (r % 2 == 1) iter(HC, t, false, sB, sA, pA, pB, kb_w, kb_r, vb_w, vb_r);
+    else iter(HC, t, false, sA, sB, pB, pA, kb_w, kb_r, vb_w, vb_r);
   };
-  // The key loop; with ping-pong, each wave group gets its own copy.
-  auto loop = [&](auto GC) __attribute__((always_inline)) {
-    if (T > 0) iter(GC, 0, true, sA, sB, pB, pA, kbuf[0], kbuf[1], vbuf[NBUF - 2], vbuf[NBUF - 1]);
-    int t = 1;
-    for (; t + NBUF <= T; t += NBUF) {
-      step(GC, t, IC<1 % NBUF>{});
-      step(GC, t + 1, IC<2 % NBUF>{});
-      if constexpr (NBUF == 4) {
-        step(GC, t + 2, IC<3>{});
-        step(GC, t + 3, IC<0>{});
-      }
-    }
-    if (t < T) step(GC, t, IC<1 % NBUF>{});
+  // The key loop.  Steps of the unrolled body all have a next tile; the last
+  // (up to NBUF) steps do not know that at compile time.
+  if (T > 0) iter(IC<0>{}, 0, true, sA, sB, pB, pA, kbuf[0], kbuf[1], vbuf[NBUF - 2], vbuf[NBUF - 1]);
+  int t = 1;
+  for (; t + NBUF < T; t += NBUF) {
+    step(IC<1>{}, t, IC<1 % NBUF>{});
+    step(IC<1>{}, t + 1, IC<2 % NBUF>{});
     if constexpr (NBUF == 4) {
-      if (t + 1 < T) step(GC, t + 1, IC<2>{});
-      if (t + 2 < T) step(GC, t + 2, IC<3>{});
+      step(IC<1>{}, t + 2, IC<3>{});
+      step(IC<1>{}, t + 3, IC<0>{});
     }
-  };
-  if constexpr (PP) {
-    if (wave < 4) loop(IC<0>{});
-    else loop(IC<1>{});
-  } else {
-    loop(IC<0>{});
+  }
+  if (t < T) step(IC<0>{}, t, IC<1 % NBUF>{});
+  if (t + 1 < T) step(IC<0>{}, t + 1, IC<2 % NBUF>{});
+  if constexpr (NBUF == 4) {
+    if (t + 2 < T) step(IC<0>{}, t + 2, IC<3>{});
+    if (t + 3 < T) step(IC<0>{}, t + 3, IC<0>{});
   }
   if (T >= 1) {
     u32x4_t vf[CB][NT16];
@@ -771,11 +726,10 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t st) {
 template <int T_, int D, int BN, int NW, int NBUF, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwdp_t(const FwdParams& p, hipStream_t st) {
   constexpr int BM = NW * 32;
-  constexpr bool PP = NW == 8 && kPrefillPP;
   FwdParams q = p;
   q.n_qt = (p.s_q + BM - 1) / BM;
   const int64_t grid = (int64_t)q.n_qt * p.b * p.h * p.n_splits;
-  hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, NW, NBUF, PP, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
+  hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, NW, NBUF, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
   return hipGetLastError();
 }
 

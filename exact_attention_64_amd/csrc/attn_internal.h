@@ -42,19 +42,13 @@ struct CombineParams {
 
 // Compile-time tunables (overridable with -D for sweeps).
 #ifndef ATTN_PREFILL_NW
-#define ATTN_PREFILL_NW 4   // waves per work-group of the d >= 64 prefill kernel (32 rows each)
+#define ATTN_PREFILL_NW 8   // waves per work-group of the d >= 64 prefill kernel (32 rows each)
 #endif
 #ifndef ATTN_PREFILL_BN
 #define ATTN_PREFILL_BN 32  // keys per tile of the d >= 64 prefill kernel
 #endif
 #ifndef ATTN_PREFILL_NBUF
 #define ATTN_PREFILL_NBUF 4 // LDS ring buffers per tensor (prefetch depth + 1), 2 or 4
-#endif
-#ifndef ATTN_PREFILL_PP
-#define ATTN_PREFILL_PP 1   // with 8 waves: ping-pong the matrix-core and vector halves
-#endif
-#ifndef ATTN_PREFILL_PRIO
-#define ATTN_PREFILL_PRIO 0 // raise the wave priority during the matrix-core half
 #endif
 #ifndef ATTN_DECODE_WAVES
 #define ATTN_DECODE_WAVES 4 // waves per work-group of the decode kernel
@@ -65,8 +59,6 @@ struct CombineParams {
 constexpr int kPrefillNW = ATTN_PREFILL_NW;
 constexpr int kPrefillBN = ATTN_PREFILL_BN;
 constexpr int kPrefillNBUF = ATTN_PREFILL_NBUF;
-constexpr bool kPrefillPP = ATTN_PREFILL_PP != 0;
-constexpr bool kPrefillPrio = ATTN_PREFILL_PRIO != 0;
 constexpr int kDecodeWaves = ATTN_DECODE_WAVES;
 constexpr int kDecodeBatch = ATTN_DECODE_BATCH;
 
