@@ -456,11 +456,12 @@ void fwdp_kernel(const FwdParams p) {
     koff[i] = (int64_t)row * ksr + (pc ^ Swz<D>::k(row)) * 8;
     voff[i] = (int64_t)row * vsr + (pc ^ Swz<D>::v(row)) * 8;
   }
+  // `full`: the caller knows the tile lies inside the key range.
   auto stage = [&](const unsigned short* __restrict__ G, int64_t gs, const int64_t (&goff)[WL],
-                   bool isv, int tile, char* buf) {
-    if (!loader) return;
+                   bool isv, int tile, char* buf, bool full) {
+    if (NLW < NW && !loader) return;
     const int k0 = k_lo + tile * BN;
-    if (k0 + BN <= k_hi) {
+    if (full || k0 + BN <= k_hi) {
       const unsigned short* __restrict__ Gt = G + (int64_t)k0 * gs;
 #pragma unroll
       for (int i = 0; i < WL; ++i)
@@ -577,12 +578,12 @@ void fwdp_kernel(const FwdParams p) {
   // the prologue waits for everything).
   const bool full = T > P;
   if (T > 0) {
-    stage(Kg, ksr, koff, false, 0, kbuf[0]);
-    if (T > 1) stage(Kg, ksr, koff, false, 1, kbuf[1]);
+    stage(Kg, ksr, koff, false, 0, kbuf[0], false);
+    if (T > 1) stage(Kg, ksr, koff, false, 1, kbuf[1], false);
 #pragma unroll
     for (int j = 0; j + 2 <= P; ++j) {
-      if (j + 2 < T) stage(Kg, ksr, koff, false, j + 2, kbuf[(j + 2) % NBUF]);
-      if (j < T) stage(Vg, vsr, voff, true, j, vbuf[j % NBUF]);
+      if (j + 2 < T) stage(Kg, ksr, koff, false, j + 2, kbuf[(j + 2) % NBUF], false);
+      if (j < T) stage(Vg, vsr, voff, true, j, vbuf[j % NBUF], false);
     }
   }
   asm volatile("" ::: "memory");
@@ -606,17 +607,20 @@ void fwdp_kernel(const FwdParams p) {
   // slot takes V_{t+NBUF-2}; V_{t-1} is read.  At the end, the loads of
   // K_{t+2} and V_t (issued NBUF - 1 steps earlier) must have landed; later
   // pairs may still be in flight.
-  // HC: 1 when the caller knows that tile t + 1 exists, which keeps the
-  // product/softmax block of the step free of branches (the scheduler cannot
-  // interleave across them).
+  // HC: what the caller knows at compile time.  0: nothing; 1: tile t + 1
+  // exists, which keeps the product/softmax block of the step free of branches
+  // (the scheduler cannot interleave across them); 2: interior step, where
+  // moreover both loads exist and lie inside the key range and tile t needs no
+  // mask, so the whole step is straight-line code apart from the rare rebase.
   auto iter = [&](auto HC, int t, bool first, f32x16_t (&s)[NB][RB], f32x16_t (&s_next)[NB][RB],
                   u32x4_t (&p_prev)[RB][NT16], u32x4_t (&p_cur)[RB][NT16],
                   char* kb_w, const char* kb_r, char* vb_w, const char* vb_r) __attribute__((always_inline)) {
-    if (t + P + 1 < T) stage(Kg, ksr, koff, false, t + P + 1, kb_w);
-    if (t + P - 1 < T) stage(Vg, vsr, voff, true, t + P - 1, vb_w);
-    const bool has_next = decltype(HC)::value == 1 || t + 1 < T;
+    constexpr int hc = decltype(HC)::value;
+    if (hc == 2 || t + P + 1 < T) stage(Kg, ksr, koff, false, t + P + 1, kb_w, hc == 2);
+    if (hc == 2 || t + P - 1 < T) stage(Vg, vsr, voff, true, t + P - 1, vb_w, hc == 2);
+    const bool has_next = hc >= 1 || t + 1 < T;
     const int k0 = k_lo + t * BN;
-    const bool need_mask = (k0 + BN > k_hi) || (CAUSAL && k0 + BN - 1 > qw0 + off);
+    const bool need_mask = hc != 2 && ((k0 + BN > k_hi) || (CAUSAL && k0 + BN - 1 > qw0 + off));
     u32x4_t kf[KK][NB], vf[CB][NT16];
     if (!first) read_v(vb_r, vf);
     if (need_mask) mask_tile(s, k0);
@@ -631,7 +635,7 @@ void fwdp_kernel(const FwdParams p) {
     if (__builtin_amdgcn_ballot_w64(bad) != 0) rebase(s, p_cur, ls);
     l[0] += ls[0];
     asm volatile("" ::: "memory");
-    if (t + P + 1 < T) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0((P - 1) * PAIR));
+    if (hc == 2 || t + P + 1 < T) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0((P - 1) * PAIR));
     else __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -647,10 +651,23 @@ void fwdp_kernel(const FwdParams p) {
     if constexpr (r % 2 == 1) iter(HC, t, false, sB, sA, pA, pB, kb_w, kb_r, vb_w, vb_r);
     else iter(HC, t, false, sA, sB, pB, pA, kb_w, kb_r, vb_w, vb_r);
   };
-  // The key loop.  Steps of the unrolled body all have a next tile; the last
-  // (up to NBUF) steps do not know that at compile time.
+  // The key loop.  Interior steps first: t + P + 1 < n_full (every load a full
+  // tile) and, when causal, tile t entirely at or below the diagonal of the
+  // work-group's first row.  Then steps that all have a next tile, then the
+  // last (up to NBUF) steps, which know nothing at compile time.
+  const int n_full = (k_hi - k_lo) / BN;
+  int t_clean = n_full - P - 1;
+  if (CAUSAL) t_clean = min(t_clean, (q0 + off - k_lo + 1) / BN);
   if (T > 0) iter(IC<0>{}, 0, true, sA, sB, pB, pA, kbuf[0], kbuf[1], vbuf[NBUF - 2], vbuf[NBUF - 1]);
   int t = 1;
+  for (; t + NBUF <= t_clean; t += NBUF) {
+    step(IC<2>{}, t, IC<1 % NBUF>{});
+    step(IC<2>{}, t + 1, IC<2 % NBUF>{});
+    if constexpr (NBUF == 4) {
+      step(IC<2>{}, t + 2, IC<3>{});
+      step(IC<2>{}, t + 3, IC<0>{});
+    }
+  }
   for (; t + NBUF < T; t += NBUF) {
     step(IC<1>{}, t, IC<1 % NBUF>{});
     step(IC<1>{}, t + 1, IC<2 % NBUF>{});
