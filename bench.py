@@ -8,8 +8,9 @@ One step = one pass of the whole path over resident synthetic inputs:
     compute-unit heuristic.
 ``value`` is the prefill throughput in TFLOP/s (algorithmic FLOPs: 4*d per
 visible (query, key) pair).  The decode figure (K+V bytes over the time of both
-decode launches) is reported beside it.  Kernel durations come from HIP events
-recorded on the stream the kernels run on.
+decode launches, taken between one pair of events, with L2 and the 256 MB MALL
+flushed by a 512 MiB fill before each pass) is reported beside it.  Kernel
+durations come from HIP events recorded on the stream the kernels run on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|decode]
 Prints one JSON line.
@@ -31,9 +32,11 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCES = ["exact_attention_64_amd/csrc/attn_fwd.hip", "exact_attention_64_amd/csrc/attn_decode.hip",
-                  "exact_attention_64_amd/csrc/attn_common.h"]
+                  "exact_attention_64_amd/csrc/attn_combine.hip", "exact_attention_64_amd/csrc/attn_common.h",
+                  "exact_attention_64_amd/csrc/attn_internal.h"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.md")
 CPU_ROWS_PER_HEAD = 2048  # seeded query rows per head in the CPU-baseline sample
+FLUSH_BYTES = 512 << 20   # written before each decode pass: evicts L2 and the 256 MB MALL
 
 
 def visible_pairs(w) -> int:
@@ -80,6 +83,36 @@ def cpu_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def device_facts(torch, dev):
+    """Compute-unit count, name and a measured copy bandwidth (1 GiB read + 1 GiB
+    written by torch's copy kernel, best of three) for context."""
+    props = torch.cuda.get_device_properties(dev)
+    n = 1 << 30
+    src = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    best = 1e30
+    for _ in range(4):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del src, dst
+    return {"name": getattr(props, "gcnArchName", props.name), "compute_units": props.multi_processor_count,
+            "copy_gbs": round(2 * n / (best * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """Time the float64 oracle on a bounded sample of the prefill workload: whole
     heads' worth of seeded query rows until about ``budget_s`` seconds of work."""
@@ -115,7 +148,8 @@ def cpu_baseline(w, budget_s: float = 12.0):
         "kind": "oracle",
         "sample": (f"float64 NumPy oracle, {done_rows} seeded query rows ({len(rows_all[0])} per head, "
                    f"{heads} of {w.h} heads) of the causal s=16384 workload, each over its full key "
-                   f"prefix; {done_flops / 1e9:.1f} GFLOP in {elapsed:.2f} s"),
+                   f"prefix; {done_flops / 1e9:.1f} GFLOP in {elapsed:.2f} s on {cpu_model()}, "
+                   f"{len(os.sched_getaffinity(0))} cores in the affinity mask"),
         "seconds": round(elapsed, 3),
         "extrapolated_full_s": round(elapsed * flops(w) / done_flops, 1),
     }
@@ -171,6 +205,7 @@ def main():
         lpart = torch.empty((n_splits, wd.b, wd.h, wd.s_q), dtype=torch.float32, device=dev)
         Od = torch.empty_like(qd)
         Ld = torch.empty((wd.b, wd.h, wd.s_q), dtype=torch.float32, device=dev)
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -181,9 +216,12 @@ def main():
             ea.attn_fwd(qp, kp, vp, wp.scale, wp.causal, out=Op, lse=Lp)
             evs[1].record()
         if do_d:
+            # Cold caches for the decode pass: its 268 MB of K/V would otherwise
+            # partly sit in the 256 MB MALL.  The fill runs before the events,
+            # and one event pair brackets both decode launches.
+            flush.fill_(0.0)
             evs[2].record()
             ea.attn_fwd_splitkv(qd, kd, vd, n_splits, wd.scale, False, o_part=opart, lse_part=lpart)
-            evs[3].record()
             ea.attn_combine(opart, lpart, qd.dtype, out=Od, lse=Ld)
             evs[4].record()
 
@@ -210,17 +248,32 @@ def main():
         p_tf = flops(wp) / (p_ms * 1e-3) / 1e12
         res["prefill"] = dict(ms=p_ms, tflops=p_tf)
     if do_d:
-        s_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
-        c_ms = sum(e[3].elapsed_time(e[4]) for e in events) / args.steps
         d_ms = sum(e[2].elapsed_time(e[4]) for e in events) / args.steps
+        # Per-kernel durations of the two decode launches (for the roofline),
+        # from their own event pairs in a separate loop after the timed steps.
+        kev = [[E() for _ in range(4)] for _ in range(args.steps)]
+        for e in kev:
+            flush.fill_(0.0)
+            e[0].record()
+            ea.attn_fwd_splitkv(qd, kd, vd, n_splits, wd.scale, False, o_part=opart, lse_part=lpart)
+            e[1].record()
+            e[2].record()
+            ea.attn_combine(opart, lpart, qd.dtype, out=Od, lse=Ld)
+            e[3].record()
+        torch.cuda.synchronize()
+        s_ms = sum(e[0].elapsed_time(e[1]) for e in kev) / args.steps
+        c_ms = sum(e[2].elapsed_time(e[3]) for e in kev) / args.steps
         kvb = 2 * 2 * wd.b * wd.s_k * wd.h * wd.d
         res["decode"] = dict(ms=d_ms, splitkv_ms=s_ms, combine_ms=c_ms, gbs=kvb / (d_ms * 1e-3) / 1e9,
                              splitkv_gbs=kvb / (s_ms * 1e-3) / 1e9, kv_bytes=kvb, splits=n_splits)
 
-    # ---- side table: the three smaller prefill workloads (median of 20 launches each)
+    # ---- side table: the three smaller prefill workloads.  Event time per launch
+    # (median, min, mean over 200 launches for C1/C2, 20 for C3, caches flushed
+    # before each), and the host time of one call through the binding.
     side = {}
     if not args.no_small and args.only == "all":
-        for name in ("C1", "C2", "C3"):
+        flush_s = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        for name, iters in (("C1", 200), ("C2", 200), ("C3", 20)):
             w = W[name]
             q, k, v = (t.to(dev) for t in workloads.make_workload(w))
             O = torch.empty_like(q)
@@ -228,21 +281,31 @@ def main():
             for _ in range(3):
                 ea.attn_fwd(q, k, v, w.scale, w.causal, out=O, lse=L)
             ts = []
-            for _ in range(20):
+            for _ in range(iters):
+                flush_s.fill_(0.0)
                 a, b = E(), E()
                 a.record()
                 ea.attn_fwd(q, k, v, w.scale, w.causal, out=O, lse=L)
                 b.record()
                 torch.cuda.synchronize()
                 ts.append(a.elapsed_time(b))
+            torch.cuda.synchronize()
+            h0 = time.perf_counter()
+            for _ in range(iters):
+                ea.attn_fwd(q, k, v, w.scale, w.causal, out=O, lse=L)
+            host_us = (time.perf_counter() - h0) / iters * 1e6
+            torch.cuda.synchronize()
             ts.sort()
             med = ts[len(ts) // 2]
             io = 2 * w.b * w.h * w.d * (2 * w.s_q + 2 * w.s_k) + 4 * w.b * w.h * w.s_q
-            side[name] = dict(workload=w.note, us=round(med * 1e3, 2),
+            side[name] = dict(workload=w.note, us=round(med * 1e3, 2), us_min=round(ts[0] * 1e3, 2),
+                              us_mean=round(sum(ts) / len(ts) * 1e3, 2), launches=iters,
+                              host_us_per_call=round(host_us, 2),
                               tflops=round(flops(w) / (med * 1e-3) / 1e12, 2),
                               io_gbs=round(io / (med * 1e-3) / 1e9, 1),
                               frac_mfma=round(flops(w) / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
             del q, k, v, O, L
+        del flush_s
 
     out = {
         "metric": "attn fwd TFLOP/s (prefill) & decode K/V GB/s, % of MI355X MFMA/HBM peak",
@@ -269,7 +332,7 @@ def main():
             "bound": "mfma", "achieved": round(p["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4),
             "traffic": read_traffic("prefill"),
-            "kernel": "fwd_kernel (attn_fwd)", "avg_launch_ms": round(p["ms"], 4),
+            "kernel": "fwdp_kernel (attn_fwd, d >= 64 prefill)", "avg_launch_ms": round(p["ms"], 4),
             "flops_per_launch": flops(wp),
         }
     if do_d:
@@ -282,7 +345,7 @@ def main():
         rd = {
             "bound": "hbm", "achieved": round(dd["splitkv_gbs"], 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(dd["splitkv_gbs"] / PEAK_HBM_GBS, 4),
-            "traffic": read_traffic("decode"), "kernel": "split-KV kernel (attn_fwd_splitkv)",
+            "traffic": read_traffic("decode"), "kernel": "decode_kernel (attn_fwd_splitkv, s_q = 1)",
             "avg_launch_ms": round(dd["splitkv_ms"], 4), "bytes_per_launch": dd["kv_bytes"],
         }
         if do_p:
@@ -296,6 +359,8 @@ def main():
             out["roofline"] = rd
     if side:
         out["other_workloads"] = side
+    if args.only == "all" and not args.no_small:
+        out["device"] = device_facts(torch, dev)
     if not args.no_cpu and do_p:
         out["cpu_baseline"] = cpu_baseline(wp)
     print(json.dumps(out), flush=True)

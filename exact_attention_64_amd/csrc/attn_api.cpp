@@ -112,8 +112,7 @@ void fill_params(const attn_args* a, attn::FwdParams* p) {
 }
 
 bool grid_ok(const attn_args* a, int64_t n_splits) {
-  const int64_t bm = attn::fwd_rows_per_block((int)a->d, (int)a->s_q);
-  const int64_t grid = ceil_div(a->s_q, bm) * a->b * a->h * n_splits;
+  const int64_t grid = attn::fwd_groups_per_split(a->b, a->h, a->s_q, (int)a->d) * n_splits;
   return grid <= 0x7fffffff;
 }
 
@@ -156,8 +155,9 @@ attn_status attn_num_splits_for(int64_t b, int64_t h, int64_t s_q, int64_t s_k, 
   if (st != ATTN_OK) return st;
   if (!headdim_ok(d)) return ATTN_E_HEADDIM;
   if (num_cus < 1) return ATTN_E_DEVICE;
-  // Parallel work without splitting: one work-group per (b, h, query row block).
-  const int64_t work = b * h * ceil_div(s_q, attn::fwd_rows_per_block((int)d, (int)s_q));
+  // Parallel work without splitting: work-groups per split (one per (b, h, query
+  // row block), or per group of heads for a single query row).
+  const int64_t work = attn::fwd_groups_per_split(b, h, s_q, (int)d);
   int64_t n = 1;
   if (work < num_cus) {
     // About one work-group per compute unit (measured best for the one-row

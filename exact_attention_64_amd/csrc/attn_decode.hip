@@ -11,12 +11,15 @@ namespace attn {
 // idle on a single query row (the issue's reply makes the same point: decode
 // speed is close to a memory copy, so spare compute does not matter).
 //
-// Work-group = NWV waves on one (b, h, split); wave w takes a contiguous quarter
-// of the split's keys.  Lane layout: a key row (D elements) is read by LPH = D/8
-// lanes, 16 bytes each, so one wave load covers KPI = 64/LPH consecutive keys.
-// Each group of LPH lanes ("slot") runs its own online softmax over the keys it
-// reads; the NWV*KPI slot states are merged through LDS at the end with the same
-// max-subtracted rule as the combine.
+// Work-group = kDecodeHeads waves; wave w streams head 4g + w (of the flattened
+// b*h heads) over the whole key range of one split, so the work-group reads the
+// rows of adjacent heads together: 1 KB of contiguous K (and V) per key at
+// d = 128, instead of 256-byte pieces 4 KB apart.  Lane layout: a key row (D
+// elements) is read by LPH = D/8 lanes, 16 bytes each, so one wave load covers
+// KPI = 64/LPH consecutive keys.  Each group of LPH lanes ("slot") runs its own
+// online softmax over the keys it reads; at the end the KPI slot states of the
+// wave are merged by a butterfly of lane shuffles with the max-subtracted rule
+// of the combine.  No LDS, no barriers.
 template <int LPH>
 __device__ __forceinline__ float slot_sum(float x) {
   // all-reduce over the LPH consecutive lanes of a slot (DPP within a row of 16)
@@ -27,25 +30,23 @@ __device__ __forceinline__ float slot_sum(float x) {
   return x;
 }
 
-template <int T_, int D, int NWV, bool SPLIT>
-__global__ __launch_bounds__(NWV * 64) void decode_kernel(const FwdParams p) {
+template <int T_, int D, bool SPLIT>
+__global__ __launch_bounds__(kDecodeHeads * 64) void decode_kernel(const FwdParams p) {
   using Tt = Ty<T_>;
   using Dt = Dot<T_>;
   constexpr int LPH = D / 8;        // lanes per key row
-  constexpr int KPI = 64 / LPH;     // keys per wave load
+  constexpr int KPI = 64 / LPH;     // keys per wave load (= slots per wave)
   constexpr int U = kDecodeBatch;   // wave loads per tensor in one batch
-  constexpr int NS = NWV * KPI;     // slot states merged at the end
 
-  __shared__ float red_m[NS], red_l[NS];
-  __shared__ __attribute__((aligned(16))) float red_o[NS][D];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int slot = lane / LPH;
   const int dc = lane % LPH;
-  const int split = blockIdx.x;
-  const int bh = blockIdx.y;
+  // 1-D grid, split fastest: work-group g covers split g % n_splits of head
+  // group g / n_splits.
+  const int split = blockIdx.x % p.n_splits;
+  const int bh = (blockIdx.x / p.n_splits) * kDecodeHeads + wave;
+  if (bh >= p.b * p.h) return;      // the whole wave; the kernel has no barriers
   const int bb = bh / p.h;
   const int hh = bh - bb * p.h;
 
@@ -54,8 +55,7 @@ __global__ __launch_bounds__(NWV * 64) void decode_kernel(const FwdParams p) {
     k_lo = (int)(((int64_t)split * p.s_k) / p.n_splits);
     k_hi = (int)(((int64_t)(split + 1) * p.s_k) / p.n_splits);
   }
-  const int ws = k_lo + (int)(((int64_t)(k_hi - k_lo) * wave) / NWV);
-  const int we = k_lo + (int)(((int64_t)(k_hi - k_lo) * (wave + 1)) / NWV);
+  const int ws = k_lo, we = k_hi;
 
   u32x4_t q = {0u, 0u, 0u, 0u};
   if (!p.zero_q) {
@@ -125,54 +125,52 @@ __global__ __launch_bounds__(NWV * 64) void decode_kernel(const FwdParams p) {
     consume(kb1, vb1, j0 + STEP);
   }
 
-  // merge the NS slot states
-  const int st = wave * KPI + slot;
-  if (dc == 0) {
-    red_m[st] = m;
-    red_l[st] = l;
+  // Merge the KPI slot states of the wave: butterfly over the slot index
+  // (partner lane = lane ^ (LPH << k)), identical states in every slot after.
+#pragma unroll
+  for (int sh = LPH; sh < 64; sh <<= 1) {
+    const float m2 = __shfl_xor(m, sh);
+    const float l2 = __shfl_xor(l, sh);
+    const float M = fmaxf(m, m2);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    const float a1 = __builtin_amdgcn_exp2f(m - Mu), a2 = __builtin_amdgcn_exp2f(m2 - Mu);
+    l = a1 * l + a2 * l2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = a1 * o[e] + a2 * __shfl_xor(o[e], sh);
+    m = M;
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) red_o[st][dc * 8 + e] = o[e];
-  __syncthreads();
-  if (tid < D / 4) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) M = fmaxf(M, red_m[i]);
-    const float Ms = M == -INFINITY ? 0.f : M;
-    float L = 0.f;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const float w = __builtin_amdgcn_exp2f(red_m[i] - Ms);
-      L += w * red_l[i];
-      acc += w * *(const f32x4_t*)&red_o[i][tid * 4];
-    }
-    const bool has = L > 0.f;
-    const float inv = has ? 1.f / L : 0.f;
-    const float lse = has ? (Ms + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
-    acc *= inv;
+  const bool has = l > 0.f;
+  const float inv = has ? 1.f / l : 0.f;
+  const float lse = has ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+  if (slot == 0) {
     if (SPLIT) {
       const int64_t rowi = ((int64_t)split * p.b + bb) * p.h + hh;  // s_q == 1
-      *(f32x4_t*)(p.o_part + rowi * D + tid * 4) = acc;
-      if (tid == 0) p.lse_part[rowi] = lse;
+      float* op = p.o_part + rowi * D + dc * 8;
+      f32x4_t x0 = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+      f32x4_t x1 = {o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+      *(f32x4_t*)op = x0;
+      *(f32x4_t*)(op + 4) = x1;
+      if (dc == 0) p.lse_part[rowi] = lse;
     } else {
-      unsigned short* op = (unsigned short*)p.o + (int64_t)bb * p.os[0] + (int64_t)hh * p.os[2];
-      u32x2_t x = {Tt::pack2(acc[0], acc[1]), Tt::pack2(acc[2], acc[3])};
-      *(u32x2_t*)(op + tid * 4) = x;
-      if (tid == 0 && p.lse) p.lse[(int64_t)bb * p.h + hh] = lse;
+      unsigned short* op = (unsigned short*)p.o + (int64_t)bb * p.os[0] + (int64_t)hh * p.os[2] + dc * 8;
+      u32x4_t x = {Tt::pack2(o[0] * inv, o[1] * inv), Tt::pack2(o[2] * inv, o[3] * inv),
+                   Tt::pack2(o[4] * inv, o[5] * inv), Tt::pack2(o[6] * inv, o[7] * inv)};
+      *(u32x4_t*)op = x;
+      if (dc == 0 && p.lse) p.lse[(int64_t)bb * p.h + hh] = lse;
     }
   }
 }
 
 template <int T_, bool SPLIT>
 static hipError_t launch_decode_t(const FwdParams& p, hipStream_t st) {
-  constexpr int NWV = kDecodeWaves;
-  const dim3 grid((unsigned)p.n_splits, (unsigned)(p.b * p.h));
+  const int64_t groups = ((int64_t)p.b * p.h + kDecodeHeads - 1) / kDecodeHeads;
+  const dim3 grid((unsigned)(groups * p.n_splits));
+  const dim3 block(kDecodeHeads * 64);
   switch (p.d) {
-    case 16: hipLaunchKernelGGL((decode_kernel<T_, 16, NWV, SPLIT>), grid, dim3(NWV * 64), 0, st, p); break;
-    case 32: hipLaunchKernelGGL((decode_kernel<T_, 32, NWV, SPLIT>), grid, dim3(NWV * 64), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((decode_kernel<T_, 64, NWV, SPLIT>), grid, dim3(NWV * 64), 0, st, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<T_, 128, NWV, SPLIT>), grid, dim3(NWV * 64), 0, st, p); break;
+    case 16: hipLaunchKernelGGL((decode_kernel<T_, 16, SPLIT>), grid, block, 0, st, p); break;
+    case 32: hipLaunchKernelGGL((decode_kernel<T_, 32, SPLIT>), grid, block, 0, st, p); break;
+    case 64: hipLaunchKernelGGL((decode_kernel<T_, 64, SPLIT>), grid, block, 0, st, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<T_, 128, SPLIT>), grid, block, 0, st, p); break;
   }
   return hipGetLastError();
 }

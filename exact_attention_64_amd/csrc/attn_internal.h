@@ -50,8 +50,8 @@ struct CombineParams {
 #ifndef ATTN_PREFILL_NBUF
 #define ATTN_PREFILL_NBUF 4 // LDS ring buffers per tensor (prefetch depth + 1), 2 or 4
 #endif
-#ifndef ATTN_DECODE_WAVES
-#define ATTN_DECODE_WAVES 4 // waves per work-group of the decode kernel
+#ifndef ATTN_DECODE_HEADS
+#define ATTN_DECODE_HEADS 4 // heads (one wave each) per work-group of the decode kernel
 #endif
 #ifndef ATTN_DECODE_BATCH
 #define ATTN_DECODE_BATCH 8 // wave loads per tensor per batch in the decode kernel
@@ -59,7 +59,7 @@ struct CombineParams {
 constexpr int kPrefillNW = ATTN_PREFILL_NW;
 constexpr int kPrefillBN = ATTN_PREFILL_BN;
 constexpr int kPrefillNBUF = ATTN_PREFILL_NBUF;
-constexpr int kDecodeWaves = ATTN_DECODE_WAVES;
+constexpr int kDecodeHeads = ATTN_DECODE_HEADS;
 constexpr int kDecodeBatch = ATTN_DECODE_BATCH;
 
 // Query rows covered by one work-group for head dim d and s_q query rows: the
@@ -67,6 +67,13 @@ constexpr int kDecodeBatch = ATTN_DECODE_BATCH;
 // (d >= 64) or 4 x 32 rows (d <= 32).
 inline int fwd_rows_per_block(int d, int s_q) {
   return s_q == 1 ? 1 : (d >= 64 ? kPrefillNW * 32 : 4 * 32);
+}
+// Work-groups per split: the decode kernel (s_q == 1) puts kDecodeHeads heads in
+// one work-group; the prefill kernel one (b, h, query row block) per work-group.
+inline int64_t fwd_groups_per_split(int64_t b, int64_t h, int64_t s_q, int d) {
+  if (s_q == 1) return (b * h + kDecodeHeads - 1) / kDecodeHeads;
+  const int64_t bm = fwd_rows_per_block(d, (int)s_q);
+  return b * h * ((s_q + bm - 1) / bm);
 }
 
 // Fused / split-KV prefill kernel (s_q >= 1; used for s_q > 1).

@@ -108,11 +108,13 @@ typedef struct {
 /* Fused forward (Lab Notes 07 sections 3.1-3.3): O and LSE in one kernel. */
 attn_status attn_fwd(const attn_args *args, void *stream);
 
-/* Split count for flash-decoding on `device` (issue #1248): 1 when
- * b*h*ceil(s_q/rows_per_block) already covers the compute units (rows_per_block
- * is 1 for a single query row, else the prefill kernel's row block), otherwise
- * enough splits to give each compute unit about one work-group, capped by
- * ceil(s_k/64) and ATTN_MAX_SPLITS.  Writes the count to *n_out. */
+/* Split count for flash-decoding on `device` (issue #1248): 1 when the
+ * work-groups of one split already cover the compute units, otherwise enough
+ * splits to give each compute unit about one work-group, capped by
+ * ceil(s_k/64) and ATTN_MAX_SPLITS.  Work-groups per split: ceil(b*h/4) for a
+ * single query row (four heads per work-group), else
+ * b*h*ceil(s_q/rows_per_block) with the prefill kernel's row block.  Writes the
+ * count to *n_out. */
 attn_status attn_num_splits(int64_t b, int64_t h, int64_t s_q, int64_t s_k, int64_t d,
                             int device, int32_t *n_out);
 

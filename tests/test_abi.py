@@ -152,11 +152,16 @@ def test_num_splits_device_error():
 # --------------------------------------------------------- heuristic ----
 
 def test_heuristic_no_split_with_enough_work():
-    # issue #1248: 8 batches x 48 heads = 384 pieces of work already cover the
-    # compute units, so the heuristic does not split.
-    for s_q in (1, 4, 10):
+    # issue #1248: when the work-groups of one split already cover the compute
+    # units, the heuristic does not split.  8 batches x 48 heads with a few
+    # query rows: 384 work-groups on 256 compute units.
+    for s_q in (4, 10):
         assert ea.attn_num_splits_for(8, 48, s_q, 4096, 128, 256) == 1
     assert ea.attn_num_splits_for(4, 32, 512, 512, 128, 256) == 1
+    # a single query row packs four heads per work-group: 8 x 128 heads give
+    # 256 work-groups, 8 x 48 only 96, which the heuristic splits three ways
+    assert ea.attn_num_splits_for(8, 128, 1, 4096, 128, 256) == 1
+    assert ea.attn_num_splits_for(8, 48, 1, 4096, 128, 256) == 3
 
 
 def test_heuristic_splits_small_decode():
@@ -169,7 +174,7 @@ def test_heuristic_splits_small_decode():
 
 def test_heuristic_monotone_in_work():
     prev = 10 ** 9
-    for bh in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512):
+    for bh in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
         n = ea.attn_num_splits_for(1, bh, 1, 65536, 128, 256)
         assert n <= prev
         prev = n
