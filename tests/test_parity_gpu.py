@@ -168,6 +168,48 @@ def test_splitkv_partials_and_combine(case, causal):
     assert (O1.float() - O.float()).abs().max().item() <= TOL_O[dt]
 
 
+DECODE_CASES = [
+    # dtype, b, h, s_k, d, splits: one query row through the decode kernel, which
+    # packs four heads of the flattened b*h into one work-group
+    ("bf16", 3, 5, 3000, 128, 37),   # 15 heads: the last work-group has 3 waves
+    ("fp16", 2, 3, 1500, 64, 200),   # many splits: the combine loads them in chunks
+    ("bf16", 1, 7, 999, 32, 5),
+    ("fp16", 2, 2, 513, 16, 64),
+    ("bf16", 5, 1, 4097, 128, 1),    # work-groups span batch entries
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[f"{c[0]}-b{c[1]}-h{c[2]}-k{c[3]}-d{c[4]}-n{c[5]}" for c in DECODE_CASES])
+def test_decode_head_groups(case):
+    dt, b, h, s_k, d, n = case
+    say("attn_decode", case)
+    q, k, v = workloads.make_qkv(b, 1, s_k, h, d, dt, seed=11)
+    scale = 1 / math.sqrt(d)
+    qd, kd, vd = upload(q, k, v)
+    O_ref, L_ref = oracle.attention(*host64(q, k, v), scale, False)
+    O, L = ea.attn_decode(qd, kd, vd, num_splits=n, softmax_scale=scale)
+    torch.cuda.synchronize()
+    check(O, L, O_ref, L_ref, dt, f"{case} split")
+    O1, L1 = ea.attn_fwd(qd, kd, vd, softmax_scale=scale)
+    torch.cuda.synchronize()
+    check(O1, L1, O_ref, L_ref, dt, f"{case} fused")
+
+
+def test_decode_packed_kv_cache_views():
+    # K and V as strided views into one packed (b, s, 2, h, d) cache
+    say("attn_decode packed KV views")
+    g = torch.Generator().manual_seed(13)
+    b, s_k, h, d = 2, 2049, 6, 128
+    kv = torch.randn((b, s_k, 2, h, d), generator=g).to(torch.bfloat16)
+    q = torch.randn((b, 1, h, d), generator=g).to(torch.bfloat16)
+    k, v = kv[:, :, 0], kv[:, :, 1]
+    O_ref, L_ref = oracle.attention(*host64(q, k.contiguous(), v.contiguous()), 0.1, False)
+    kvd = kv.to(DEV)
+    O, L = ea.attn_decode(q.to(DEV), kvd[:, :, 0], kvd[:, :, 1], softmax_scale=0.1)
+    torch.cuda.synchronize()
+    check(O, L, O_ref, L_ref, "bf16", "packed KV")
+
+
 def test_combine_identical_splits_adds_ln2():
     say("attn_combine identical splits")
     g = torch.Generator().manual_seed(3)
