@@ -45,6 +45,7 @@ class AttnArgs(ctypes.Structure):
         ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
         ("q_stride", I64x3), ("k_stride", I64x3), ("v_stride", I64x3), ("o_stride", I64x3),
         ("softmax_scale", ctypes.c_float),
+        ("h_kv", ctypes.c_int64),
     ]
 
 
@@ -119,9 +120,11 @@ def make_args(q, k, v, softmax_scale=None, causal=False, out=None, lse=None) -> 
     if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share dtype float16 or bfloat16")
     b, s_q, h, d = q.shape
-    s_k = k.shape[1]
-    if tuple(k.shape) != (b, s_k, h, d) or tuple(v.shape) != (b, s_k, h, d):
-        raise ValueError(f"k and v must be (b, s_k, h, d) = ({b}, s_k, {h}, {d})")
+    if k.dim() != 4:
+        raise ValueError("k and v must be 4-D (b, s_k, h_kv, d)")
+    s_k, h_kv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (b, s_k, h_kv, d) or tuple(v.shape) != (b, s_k, h_kv, d) or h_kv < 1 or h % h_kv != 0:
+        raise ValueError(f"k and v must be (b, s_k, h_kv, d) = ({b}, s_k, h_kv, {d}) with h_kv dividing {h}")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
     a = AttnArgs()
@@ -140,6 +143,7 @@ def make_args(q, k, v, softmax_scale=None, causal=False, out=None, lse=None) -> 
             raise ValueError("lse must be a contiguous float32 (b, h, s_q) tensor")
         a.lse = lse.data_ptr()
     a.softmax_scale = float(softmax_scale)
+    a.h_kv = h_kv
     return a
 
 

@@ -39,6 +39,7 @@ attn_status check_args(const attn_args* a, bool need_o) {
   if (a->dtype != ATTN_FP16 && a->dtype != ATTN_BF16) return ATTN_E_DTYPE;
   attn_status st = check_shape(a->b, a->h, a->s_q, a->s_k);
   if (st != ATTN_OK) return st;
+  if (a->h_kv < 0 || a->h_kv > a->h || (a->h_kv > 0 && a->h % a->h_kv != 0)) return ATTN_E_SHAPE;
   if (!headdim_ok(a->d)) return ATTN_E_HEADDIM;
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v)) return ATTN_E_LAYOUT;
   if (!strides_ok(a->q_stride) || !strides_ok(a->k_stride) || !strides_ok(a->v_stride)) return ATTN_E_LAYOUT;
@@ -102,6 +103,7 @@ void fill_params(const attn_args* a, attn::FwdParams* p) {
   p->s_k = (int)a->s_k;
   p->d = (int)a->d;
   p->n_splits = 1;
+  p->g = a->h_kv > 0 ? (int)(a->h / a->h_kv) : 1;
   const float s = a->softmax_scale;
   // The kernels work in base 2 with log2(e) folded into the scale.  A negative
   // scale is applied by negating Q on load; a zero scale by zeroing Q (then every

@@ -62,8 +62,9 @@ __global__ __launch_bounds__(kDecodeHeads * 64) void decode_kernel(const FwdPara
     q = *(const u32x4_t*)((const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2] + dc * 8);
     if (p.neg_q) q ^= 0x80008000u;
   }
-  const unsigned short* __restrict__ Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hh * p.ks[2] + dc * 8;
-  const unsigned short* __restrict__ Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hh * p.vs[2] + dc * 8;
+  const int hk = hh / p.g;  // K/V head of this query head
+  const unsigned short* __restrict__ Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hk * p.ks[2] + dc * 8;
+  const unsigned short* __restrict__ Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hk * p.vs[2] + dc * 8;
   const int64_t ksr = p.ks[1], vsr = p.vs[1];
   const float c = p.scale_log2;
 

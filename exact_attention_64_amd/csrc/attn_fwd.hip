@@ -134,8 +134,9 @@ void fwdp_kernel(const FwdParams p) {
   const int T = k_hi > k_lo ? (k_hi - k_lo + BN - 1) / BN : 0;
 
   const unsigned short* __restrict__ Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
-  const unsigned short* __restrict__ Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hh * p.ks[2];
-  const unsigned short* __restrict__ Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hh * p.vs[2];
+  const int hk = hh / p.g;  // K/V head of this query head
+  const unsigned short* __restrict__ Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hk * p.ks[2];
+  const unsigned short* __restrict__ Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hk * p.vs[2];
   const int64_t ksr = p.ks[1], vsr = p.vs[1];
   const int qw0 = q0 + wave * 32;
 

@@ -28,6 +28,7 @@ struct FwdParams {
   float scale_log2; // |softmax_scale| * log2(e)  (1 when zero_q)
   int neg_q;        // softmax_scale < 0: Q is negated on load
   int zero_q;       // softmax_scale == 0: Q is treated as zero
+  int g;            // query heads per K/V head: query head hh reads K/V head hh / g
 };
 
 struct CombineParams {

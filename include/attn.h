@@ -21,9 +21,11 @@
  *     zero and negative values included, is accepted.
  *
  * Layout
- *   Q is (b, s_q, h, d); K, V are (b, s_k, h, d); O is (b, s_q, h, d): the
+ *   Q is (b, s_q, h, d); K, V are (b, s_k, h_kv, d); O is (b, s_q, h, d): the
  *   (batch, seq, heads, dim) order that flash_attn_func consumes in Lab Notes 07
- *   section 2.  The d dimension is contiguous (stride 1).  The other three
+ *   section 2.  h_kv == h (or 0) is plain multi-head attention; a smaller h_kv
+ *   lets groups of h / h_kv consecutive query heads share one K/V head, the
+ *   several "q heads" over one K tile asked about in issue #1248.  The d dimension is contiguous (stride 1).  The other three
  *   dimensions take arbitrary non-negative element strides (b, s, h order), each
  *   a multiple of 8 elements, so flattened (b, s, h*d) tensors and views are
  *   accepted without copies.  Base pointers must be 16-byte aligned.  LSE is a
@@ -70,7 +72,8 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_E_NULL = -1,    /* a required pointer (or the args struct) is NULL */
   ATTN_E_DTYPE = -2,   /* dtype is not ATTN_FP16 / ATTN_BF16 */
-  ATTN_E_SHAPE = -3,   /* b, h, s_q or s_k < 1, or a size beyond the limits below */
+  ATTN_E_SHAPE = -3,   /* b, h, s_q or s_k < 1, a size beyond the limits below, or
+                          h_kv < 0, h_kv > h, or h not a multiple of h_kv */
   ATTN_E_HEADDIM = -4, /* d not in {16, 32, 64, 128}; inputs are never padded */
   ATTN_E_LAYOUT = -5,  /* misaligned pointer, negative stride, or a stride that is
                           not a multiple of 8 elements */
@@ -103,6 +106,8 @@ typedef struct {
   int64_t v_stride[3];
   int64_t o_stride[3];  /* unused by attn_fwd_splitkv */
   float softmax_scale;
+  int64_t h_kv;         /* K/V heads: 0 means h; else h must be a multiple of h_kv
+                           and query head hh reads K/V head hh / (h / h_kv) */
 } attn_args;
 
 /* Fused forward (Lab Notes 07 sections 3.1-3.3): O and LSE in one kernel. */

@@ -19,12 +19,14 @@ def _get(x, *idx):
 
 
 def attention_brute(q, k, v, scale: float, causal: bool):
-    """q (b,s_q,h,d), k and v (b,s_k,h,d) as nested sequences or arrays.
+    """q (b,s_q,h,d), k and v (b,s_k,h_kv,d) as nested sequences or arrays; query
+    head hi uses K/V head hi // (h // h_kv).
 
     Returns (O, LSE) as nested Python lists shaped (b,s_q,h,d) and (b,h,s_q).
     """
     b, s_q, h, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
     s_k = len(k[0])
+    group = h // len(k[0][0])
     O = [[[[0.0] * d for _ in range(h)] for _ in range(s_q)] for _ in range(b)]
     LSE = [[[0.0] * s_q for _ in range(h)] for _ in range(b)]
     for bi in range(b):
@@ -36,7 +38,7 @@ def attention_brute(q, k, v, scale: float, causal: bool):
                     continue
                 scores = []
                 for j in keys:
-                    dot = math.fsum(_get(q, bi, i, hi, c) * _get(k, bi, j, hi, c)
+                    dot = math.fsum(_get(q, bi, i, hi, c) * _get(k, bi, j, hi // group, c)
                                     for c in range(d))
                     scores.append(scale * dot)
                 m = max(scores)
@@ -44,6 +46,6 @@ def attention_brute(q, k, v, scale: float, causal: bool):
                 tot = math.fsum(e)
                 for c in range(d):
                     O[bi][i][hi][c] = math.fsum(
-                        e[t] * _get(v, bi, j, hi, c) for t, j in enumerate(keys)) / tot
+                        e[t] * _get(v, bi, j, hi // group, c) for t, j in enumerate(keys)) / tot
                 LSE[bi][hi][i] = m + math.log(tot)
     return O, LSE

@@ -26,8 +26,11 @@ Readings taken where the pages are silent:
   * all arithmetic is float64 on the exact fp16/bf16 input values;
   * the scale is an explicit argument (the pages use 1/sqrt(d)).
 
-Layouts: q is (b, s_q, h, d); k and v are (b, s_k, h, d); O is (b, s_q, h, d);
-LSE is (b, h, s_q).
+Layouts: q is (b, s_q, h, d); k and v are (b, s_k, h_kv, d) with h a multiple of
+h_kv; O is (b, s_q, h, d); LSE is (b, h, s_q).  Query head hh attends with K/V
+head hh // (h / h_kv): h_kv = h is plain multi-head attention, and a smaller
+h_kv lets consecutive query heads share one K/V head (the several "q heads" over
+one K tile asked about in issue #1248).
 """
 from __future__ import annotations
 
@@ -85,6 +88,13 @@ def _as_f64(*xs):
     return [np.asarray(x, dtype=np.float64) for x in xs]
 
 
+def kv_head_of(h: int, h_kv: int) -> np.ndarray:
+    """K/V head index of every query head: hh // (h / h_kv)."""
+    if h_kv < 1 or h % h_kv:
+        raise ValueError(f"h = {h} is not a multiple of h_kv = {h_kv}")
+    return np.arange(h) // (h // h_kv)
+
+
 def attention(q, k, v, scale: float, causal: bool):
     """Exact attention forward. Returns (O (b,s_q,h,d), LSE (b,h,s_q)), float64.
 
@@ -93,12 +103,13 @@ def attention(q, k, v, scale: float, causal: bool):
     q, k, v = _as_f64(q, k, v)
     b, s_q, h, d = q.shape
     s_k = k.shape[1]
+    kv = kv_head_of(h, k.shape[2])
     mask = visible_mask(s_q, s_k, causal)
     O = np.zeros((b, s_q, h, d))
     LSE = np.zeros((b, h, s_q))
     for bi in range(b):
-        o, lse = _attend(q[bi].transpose(1, 0, 2), k[bi].transpose(1, 0, 2),
-                         v[bi].transpose(1, 0, 2), scale, mask)
+        o, lse = _attend(q[bi].transpose(1, 0, 2), k[bi][:, kv].transpose(1, 0, 2),
+                         v[bi][:, kv].transpose(1, 0, 2), scale, mask)
         O[bi] = o.transpose(1, 0, 2)
         LSE[bi] = lse
     return O, LSE
@@ -114,6 +125,7 @@ def attention_rows(q, k, v, scale: float, causal: bool, rows):
     q, k, v = _as_f64(q, k, v)
     b, s_q, h, d = q.shape
     s_k = k.shape[1]
+    kv = kv_head_of(h, k.shape[2])
     n = len(rows[0])
     O = np.zeros((b, h, n, d))
     LSE = np.zeros((b, h, n))
@@ -121,7 +133,7 @@ def attention_rows(q, k, v, scale: float, causal: bool, rows):
         r = np.asarray(rows[hi], dtype=np.int64)
         mask = visible_mask(s_q, s_k, causal, r)
         for bi in range(b):
-            o, lse = _attend(q[bi, r, hi, :], k[bi, :, hi, :], v[bi, :, hi, :], scale, mask)
+            o, lse = _attend(q[bi, r, hi, :], k[bi, :, kv[hi], :], v[bi, :, kv[hi], :], scale, mask)
             O[bi, hi] = o
             LSE[bi, hi] = lse
     return O, LSE
@@ -144,6 +156,7 @@ def attention_split(q, k, v, scale: float, causal: bool, bounds):
     q, k, v = _as_f64(q, k, v)
     b, s_q, h, d = q.shape
     s_k = k.shape[1]
+    kv = kv_head_of(h, k.shape[2])
     full = visible_mask(s_q, s_k, causal)
     n = len(bounds)
     O = np.zeros((n, b, h, s_q, d))
@@ -151,8 +164,8 @@ def attention_split(q, k, v, scale: float, causal: bool, bounds):
     for si, (lo, hi) in enumerate(bounds):
         mask = full[:, lo:hi]
         for bi in range(b):
-            o, lse = _attend(q[bi].transpose(1, 0, 2), k[bi, lo:hi].transpose(1, 0, 2),
-                             v[bi, lo:hi].transpose(1, 0, 2), scale, mask)
+            o, lse = _attend(q[bi].transpose(1, 0, 2), k[bi, lo:hi][:, kv].transpose(1, 0, 2),
+                             v[bi, lo:hi][:, kv].transpose(1, 0, 2), scale, mask)
             O[si, bi] = o
             LSE[si, bi] = lse
     return O, LSE

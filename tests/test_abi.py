@@ -42,9 +42,10 @@ def test_struct_layout_matches_c(tmp_path):
 #include <stdio.h>
 #include "attn.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(attn_args), offsetof(attn_args, b),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(attn_args), offsetof(attn_args, b),
          offsetof(attn_args, q), offsetof(attn_args, lse), offsetof(attn_args, q_stride),
-         offsetof(attn_args, o_stride), offsetof(attn_args, softmax_scale), sizeof(attn_status));
+         offsetof(attn_args, o_stride), offsetof(attn_args, softmax_scale),
+         offsetof(attn_args, h_kv), sizeof(attn_status));
   return 0;
 }
 ''')
@@ -55,7 +56,7 @@ int main(void) {
                                            check=True).stdout.split()]
     A = _lib.AttnArgs
     want = [ctypes.sizeof(A), A.b.offset, A.q.offset, A.lse.offset, A.q_stride.offset,
-            A.o_stride.offset, A.softmax_scale.offset, 4]
+            A.o_stride.offset, A.softmax_scale.offset, A.h_kv.offset, 4]
     assert got == want
 
 
@@ -89,6 +90,9 @@ BAD = [
     ("misaligned_o", dict(o=FAKE + 2), -5),
     ("stride_not_mult8", dict(k_stride=_lib.I64x3(8 * 64 * 128, 4 * 128 + 4, 128)), -5),
     ("stride_negative", dict(v_stride=_lib.I64x3(-64 * 4 * 128, 4 * 128, 128)), -5),
+    ("h_kv_negative", dict(h_kv=-1), -3),
+    ("h_kv_above_h", dict(h_kv=8), -3),
+    ("h_kv_not_divisor", dict(h_kv=3), -3),
     ("scale_nan", dict(softmax_scale=float("nan")), -6),
     ("scale_inf", dict(softmax_scale=float("inf")), -6),
 ]

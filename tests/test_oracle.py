@@ -6,7 +6,9 @@
 * closed forms: Q = 0 gives the mean of the visible V rows and LSE = ln |J(i)|;
   a single key gives V[0] and LSE = scale·q·k0; constant V columns come back;
 * invariants: rows of P sum to 1, key shift (with scores far beyond exp's range),
-  key permutation, split + reduction = unsplit, two identical splits add ln 2.
+  key permutation, split + reduction = unsplit, two identical splits add ln 2;
+* shared K/V heads (h_kv < h) = multi-head attention on K/V heads repeated
+  outside the oracle, and the brute force with the same head mapping.
 
 A mutation test plants plausible mistakes in the oracle (on the CPU) and checks
 that at least one pin catches each of them.
@@ -240,9 +242,50 @@ def pin_rows_subset():
             np.testing.assert_allclose(Lr[:, hi], L[:, hi, rows[hi]], atol=1e-14)
 
 
+def pin_gqa_is_mha_on_repeated_heads():
+    # K/V heads shared by groups of consecutive query heads: identical to plain
+    # multi-head attention on K/V whose heads are repeated group-size times
+    # (expanded here, outside the oracle), for the full, sampled-row and split forms.
+    r = np.random.default_rng(31)
+    b, s_q, s_k, h, h_kv, d = 2, 7, 9, 6, 2, 4
+    q = r.standard_normal((b, s_q, h, d))
+    k = r.standard_normal((b, s_k, h_kv, d))
+    v = r.standard_normal((b, s_k, h_kv, d))
+    ke, ve = np.repeat(k, h // h_kv, axis=2), np.repeat(v, h // h_kv, axis=2)
+    for causal in (False, True):
+        O, L = oracle.attention(q, k, v, 0.6, causal)
+        Oe, Le = oracle.attention(q, ke, ve, 0.6, causal)
+        np.testing.assert_allclose(O, Oe, atol=1e-14)
+        np.testing.assert_allclose(L, Le, atol=1e-14)
+        rows = [[0, 6], [1, 5], [2, 4], [3, 3], [4, 2], [5, 0]]
+        Or, Lr = oracle.attention_rows(q, k, v, 0.6, causal, rows)
+        Ore, Lre = oracle.attention_rows(q, ke, ve, 0.6, causal, rows)
+        np.testing.assert_allclose(Or, Ore, atol=1e-14)
+        np.testing.assert_allclose(Lr, Lre, atol=1e-14)
+        bounds = oracle.split_bounds(s_k, 3)
+        Op, Lp = oracle.attention_split(q, k, v, 0.6, causal, bounds)
+        Ope, Lpe = oracle.attention_split(q, ke, ve, 0.6, causal, bounds)
+        np.testing.assert_allclose(Op, Ope, atol=1e-14)
+        np.testing.assert_allclose(Lp, Lpe, atol=1e-14)
+
+
+def pin_gqa_brute():
+    r = np.random.default_rng(37)
+    b, s_q, s_k, h, h_kv, d = 1, 3, 5, 4, 2, 3
+    q = r.standard_normal((b, s_q, h, d))
+    k = r.standard_normal((b, s_k, h_kv, d))
+    v = r.standard_normal((b, s_k, h_kv, d))
+    for causal in (False, True):
+        O, L = oracle.attention(q, k, v, 0.8, causal)
+        Ob, Lb = attention_brute(q, k, v, 0.8, causal)
+        np.testing.assert_allclose(O, np.array(Ob), atol=1e-12)
+        np.testing.assert_allclose(L, np.array(Lb), atol=1e-12)
+
+
 PINS = [pin_golden, pin_brute, pin_torch_special_case, pin_rows_sum_to_one, pin_constant_v,
         pin_q_zero_closed_form, pin_single_key, pin_key_shift, pin_key_permutation,
-        pin_split_equals_unsplit, pin_identical_splits, pin_rows_subset]
+        pin_split_equals_unsplit, pin_identical_splits, pin_rows_subset,
+        pin_gqa_is_mha_on_repeated_heads, pin_gqa_brute]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -316,7 +359,12 @@ def _combine_unweighted(o_parts, lse_parts):
     return o_parts.mean(0), lse
 
 
+def _kv_head_modulo(h, h_kv):
+    return np.arange(h) % h_kv
+
+
 MUTANTS = {
+    "gqa_head_modulo": ("kv_head_of", _kv_head_modulo),
     "softmax_no_max": ("softmax_rows", _softmax_no_max),
     "lse_without_max": ("softmax_rows", _softmax_lse_without_max),
     "causal_top_left": ("visible_mask", _mask_top_left),

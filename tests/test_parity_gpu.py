@@ -210,6 +210,46 @@ def test_decode_packed_kv_cache_views():
     check(O, L, O_ref, L_ref, "bf16", "packed KV")
 
 
+GQA_CASES = [
+    # dtype, b, s_q, s_k, h, h_kv, d, causal: groups of h / h_kv query heads share K/V
+    ("bf16", 2, 300, 333, 6, 2, 128, True),
+    ("fp16", 1, 517, 517, 8, 1, 64, False),    # one K/V head for all queries
+    ("bf16", 2, 100, 130, 4, 2, 32, True),
+    ("fp16", 3, 50, 70, 6, 3, 16, False),
+]
+
+
+@pytest.mark.parametrize("case", GQA_CASES, ids=[f"{c[0]}-b{c[1]}-q{c[2]}-k{c[3]}-h{c[4]}-kv{c[5]}-d{c[6]}" for c in GQA_CASES])
+def test_shared_kv_heads(case):
+    dt, b, s_q, s_k, h, h_kv, d, causal = case
+    say("attn_fwd shared K/V heads", case)
+    q, k, v = workloads.make_qkv(b, s_q, s_k, h, d, dt, seed=17, h_kv=h_kv)
+    scale = 1 / math.sqrt(d)
+    O_ref, L_ref = oracle.attention(*host64(q, k, v), scale, causal)
+    O, L = run_fwd(q, k, v, scale, causal)
+    check(O, L, O_ref, L_ref, dt, f"{case} fused")
+    qd, kd, vd = upload(q, k, v)
+    O2, L2 = ea.attn_decode(qd, kd, vd, num_splits=3, softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    check(O2, L2, O_ref, L_ref, dt, f"{case} split")
+
+
+@pytest.mark.parametrize("s_q", [1, 4, 10])
+def test_multi_token_decode_48_heads(s_q):
+    # issue #1248's decode setting: batch 8, 48 query heads, 1-10 new tokens
+    # (here over 8 K/V heads and a 4096-key cache, bf16, d = 128)
+    say("multi-token decode b=8 h=48 h_kv=8 s_k=4096 s_q", s_q)
+    q, k, v = workloads.make_qkv(8, s_q, 4096, 48, 128, "bf16", seed=19, h_kv=8)
+    scale = 1 / math.sqrt(128)
+    O_ref, L_ref = oracle.attention(*host64(q, k, v), scale, True)
+    O, L = run_fwd(q, k, v, scale, True)
+    check(O, L, O_ref, L_ref, "bf16", f"s_q={s_q} fused")
+    qd, kd, vd = upload(q, k, v)
+    O2, L2 = ea.attn_decode(qd, kd, vd, softmax_scale=scale, causal=True)
+    torch.cuda.synchronize()
+    check(O2, L2, O_ref, L_ref, "bf16", f"s_q={s_q} split (heuristic)")
+
+
 def test_combine_identical_splits_adds_ln2():
     say("attn_combine identical splits")
     g = torch.Generator().manual_seed(3)

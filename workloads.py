@@ -73,16 +73,18 @@ WORKLOADS = {
 }
 
 
-def make_qkv(b: int, s_q: int, s_k: int, h: int, d: int, dtype: str, seed: int = 42):
-    """Draw q (b,s_q,h,d), k and v (b,s_k,h,d) on the CPU, rounded to ``dtype``.
+def make_qkv(b: int, s_q: int, s_k: int, h: int, d: int, dtype: str, seed: int = 42, h_kv: int = 0):
+    """Draw q (b,s_q,h,d), k and v (b,s_k,h_kv,d) on the CPU, rounded to ``dtype``
+    (h_kv = 0 means h_kv = h).
 
     Returns contiguous CPU tensors of the storage dtype.
     """
     g = torch.Generator(device="cpu").manual_seed(seed)
     td = DTYPES[dtype]
+    hk = h_kv or h
     q = torch.randn((b, s_q, h, d), generator=g, dtype=torch.float32).to(td)
-    k = torch.randn((b, s_k, h, d), generator=g, dtype=torch.float32).to(td)
-    v = torch.randn((b, s_k, h, d), generator=g, dtype=torch.float32).to(td)
+    k = torch.randn((b, s_k, hk, d), generator=g, dtype=torch.float32).to(td)
+    v = torch.randn((b, s_k, hk, d), generator=g, dtype=torch.float32).to(td)
     return q, k, v
 
 
