@@ -30,8 +30,8 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_E_NULL", -2: "ATTN_E_DTYPE", -3: "ATTN_E_SHAPE
 I64x3 = ctypes.c_int64 * 3
 
 # Every symbol include/attn.h declares.
-EXPORTS = ("attn_fwd", "attn_num_splits", "attn_num_splits_for", "attn_fwd_splitkv",
-           "attn_combine", "attn_status_str")
+EXPORTS = ("attn_fwd", "attn_num_splits", "attn_num_splits_for", "attn_num_splits_kv",
+           "attn_num_splits_kv_for", "attn_fwd_splitkv", "attn_combine", "attn_status_str")
 
 
 class AttnArgs(ctypes.Structure):
@@ -78,6 +78,10 @@ def lib():
             L.attn_num_splits.restype = ctypes.c_int32
             L.attn_num_splits_for.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int32, P(ctypes.c_int32)]
             L.attn_num_splits_for.restype = ctypes.c_int32
+            L.attn_num_splits_kv.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, P(ctypes.c_int32)]
+            L.attn_num_splits_kv.restype = ctypes.c_int32
+            L.attn_num_splits_kv_for.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int32, P(ctypes.c_int32)]
+            L.attn_num_splits_kv_for.restype = ctypes.c_int32
             L.attn_fwd_splitkv.argtypes = [P(AttnArgs), ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p]
             L.attn_fwd_splitkv.restype = ctypes.c_int32
@@ -160,16 +164,16 @@ def attn_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, stre
     return out, lse
 
 
-def attn_num_splits(b, h, s_q, s_k, d, device=None) -> int:
+def attn_num_splits(b, h, s_q, s_k, d, device=None, h_kv=0) -> int:
     n = ctypes.c_int32(0)
     dev = torch.cuda.current_device() if device is None else int(device)
-    _check(lib().attn_num_splits(b, h, s_q, s_k, d, dev, ctypes.byref(n)))
+    _check(lib().attn_num_splits_kv(b, h, h_kv, s_q, s_k, d, dev, ctypes.byref(n)))
     return n.value
 
 
-def attn_num_splits_for(b, h, s_q, s_k, d, num_cus) -> int:
+def attn_num_splits_for(b, h, s_q, s_k, d, num_cus, h_kv=0) -> int:
     n = ctypes.c_int32(0)
-    _check(lib().attn_num_splits_for(b, h, s_q, s_k, d, num_cus, ctypes.byref(n)))
+    _check(lib().attn_num_splits_kv_for(b, h, h_kv, s_q, s_k, d, num_cus, ctypes.byref(n)))
     return n.value
 
 
@@ -179,7 +183,7 @@ def attn_fwd_splitkv(q, k, v, num_splits=0, softmax_scale=None, causal=False, o_
     b, s_q, h, d = q.shape
     s_k = k.shape[1]
     if num_splits == 0:
-        num_splits = attn_num_splits(b, h, s_q, s_k, d, q.device.index)
+        num_splits = attn_num_splits(b, h, s_q, s_k, d, q.device.index, h_kv=k.shape[2])
     if o_part is None:
         o_part = torch.empty((num_splits, b, h, s_q, d), dtype=torch.float32, device=q.device)
     if lse_part is None:

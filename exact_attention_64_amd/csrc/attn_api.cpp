@@ -113,8 +113,10 @@ void fill_params(const attn_args* a, attn::FwdParams* p) {
   p->scale_log2 = s == 0.f ? 1.f : std::fabs(s) * 1.4426950408889634f;
 }
 
+int64_t group_of(const attn_args* a) { return a->h_kv > 0 ? a->h / a->h_kv : 1; }
+
 bool grid_ok(const attn_args* a, int64_t n_splits) {
-  const int64_t grid = attn::fwd_groups_per_split(a->b, a->h, a->s_q, (int)a->d) * n_splits;
+  const int64_t grid = attn::fwd_groups_per_split(a->b, a->h, group_of(a), a->s_q, (int)a->d) * n_splits;
   return grid <= 0x7fffffff;
 }
 
@@ -150,16 +152,19 @@ attn_status attn_fwd(const attn_args* a, void* stream) {
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
-attn_status attn_num_splits_for(int64_t b, int64_t h, int64_t s_q, int64_t s_k, int64_t d,
-                                int32_t num_cus, int32_t* n_out) {
+attn_status attn_num_splits_kv_for(int64_t b, int64_t h, int64_t h_kv, int64_t s_q, int64_t s_k,
+                                   int64_t d, int32_t num_cus, int32_t* n_out) {
   if (!n_out) return ATTN_E_NULL;
   attn_status st = check_shape(b, h, s_q, s_k);
   if (st != ATTN_OK) return st;
+  if (h_kv < 0 || h_kv > h || (h_kv > 0 && h % h_kv != 0)) return ATTN_E_SHAPE;
   if (!headdim_ok(d)) return ATTN_E_HEADDIM;
   if (num_cus < 1) return ATTN_E_DEVICE;
   // Parallel work without splitting: work-groups per split (one per (b, h, query
-  // row block), or per group of heads for a single query row).
-  const int64_t work = attn::fwd_groups_per_split(b, h, s_q, (int)d);
+  // row block), per group of heads for a single query row, or per (b, K/V head)
+  // when query heads sharing a K/V head are packed).
+  const int64_t g = h_kv > 0 ? h / h_kv : 1;
+  const int64_t work = attn::fwd_groups_per_split(b, h, g, s_q, (int)d);
   int64_t n = 1;
   if (work < num_cus) {
     // About one work-group per compute unit (measured best for the one-row
@@ -173,8 +178,13 @@ attn_status attn_num_splits_for(int64_t b, int64_t h, int64_t s_q, int64_t s_k, 
   return ATTN_OK;
 }
 
-attn_status attn_num_splits(int64_t b, int64_t h, int64_t s_q, int64_t s_k, int64_t d, int device,
-                            int32_t* n_out) {
+attn_status attn_num_splits_for(int64_t b, int64_t h, int64_t s_q, int64_t s_k, int64_t d,
+                                int32_t num_cus, int32_t* n_out) {
+  return attn_num_splits_kv_for(b, h, h, s_q, s_k, d, num_cus, n_out);
+}
+
+attn_status attn_num_splits_kv(int64_t b, int64_t h, int64_t h_kv, int64_t s_q, int64_t s_k, int64_t d,
+                               int device, int32_t* n_out) {
   if (!n_out) return ATTN_E_NULL;
   attn_status st = check_shape(b, h, s_q, s_k);
   if (st != ATTN_OK) return st;
@@ -183,7 +193,12 @@ attn_status attn_num_splits(int64_t b, int64_t h, int64_t s_q, int64_t s_k, int6
   st = device_info(device, &info);
   if (st != ATTN_OK) return st;
   if (!info.gfx950) return ATTN_E_DEVICE;
-  return attn_num_splits_for(b, h, s_q, s_k, d, info.cus, n_out);
+  return attn_num_splits_kv_for(b, h, h_kv, s_q, s_k, d, info.cus, n_out);
+}
+
+attn_status attn_num_splits(int64_t b, int64_t h, int64_t s_q, int64_t s_k, int64_t d, int device,
+                            int32_t* n_out) {
+  return attn_num_splits_kv(b, h, h, s_q, s_k, d, device, n_out);
 }
 
 attn_status attn_fwd_splitkv(const attn_args* a, int32_t num_splits, float* o_part, float* lse_part,

@@ -85,7 +85,10 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, const char* lds) {
                : "memory", "m0");
 }
 
-template <int T_, int D, int BN, int NW, int NBUF, bool CAUSAL, bool SPLIT>
+// PACK (query heads sharing a K/V head, few query rows): a work-group covers one
+// (batch, K/V head) and its g * s_q query rows, row r being query head
+// hk * g + r / s_q at position r % s_q, so every K/V tile serves the whole group.
+template <int T_, int D, int BN, int NW, int NBUF, bool PACK, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 64 ? 2 : 4, D >= 64 ? 2 : 4)))
 void fwdp_kernel(const FwdParams p) {
   using Tt = Ty<T_>;
@@ -114,43 +117,56 @@ void fwdp_kernel(const FwdParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int per_qt = p.b * p.h * p.n_splits;
+  const int nh = PACK ? p.h / p.g : p.h;  // heads indexed by the grid
+  const int per_qt = p.b * nh * p.n_splits;
   const int qt_rev = blockIdx.x / per_qt;
   const int rem = blockIdx.x - qt_rev * per_qt;
   const int bh = rem / p.n_splits;
   const int split = rem - bh * p.n_splits;
   const int qt = CAUSAL ? (p.n_qt - 1 - qt_rev) : qt_rev;
-  const int bb = bh / p.h;
-  const int hh = bh - bb * p.h;
+  const int bb = bh / nh;
+  const int hg = bh - bb * nh;
+  const int hk = PACK ? hg : hg / p.g;   // K/V head of the work-group
   const int q0 = qt * BM;
   const int off = p.s_k - p.s_q;
+  // This lane's row: query head my_h, position my_i (both uniform per
+  // work-group unless packed).  Position bounds for the masking decisions are
+  // exact for one head's contiguous rows and conservative when packed.
+  const int rw = q0 + wave * 32 + l32;
+  const bool row_ok = rw < (PACK ? p.g * p.s_q : p.s_q);
+  const int my_i = PACK ? rw % p.s_q : rw;
+  const int my_h = PACK ? hk * p.g + rw / p.s_q : hg;
+  const int pos_wg_lo = PACK ? 0 : q0;
+  const int pos_wg_hi = PACK ? p.s_q - 1 : q0 + BM - 1;
+  const int pos_wave_lo = PACK ? 0 : q0 + wave * 32;
+  // Packed work-groups often have waves with no rows at all (6 heads x 1 row
+  // fill one wave of eight): such a wave only loads its share of each tile.
+  const bool live = !PACK || q0 + wave * 32 < p.g * p.s_q;
 
   int k_lo = 0, k_hi = p.s_k;
   if (SPLIT) {
     k_lo = (int)(((int64_t)split * p.s_k) / p.n_splits);
     k_hi = (int)(((int64_t)(split + 1) * p.s_k) / p.n_splits);
   }
-  if (CAUSAL) k_hi = min(k_hi, q0 + BM + off);
+  if (CAUSAL) k_hi = min(k_hi, pos_wg_hi + off + 1);
   const int T = k_hi > k_lo ? (k_hi - k_lo + BN - 1) / BN : 0;
 
-  const unsigned short* __restrict__ Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
-  const int hk = hh / p.g;  // K/V head of this query head
   const unsigned short* __restrict__ Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hk * p.ks[2];
   const unsigned short* __restrict__ Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hk * p.vs[2];
   const int64_t ksr = p.ks[1], vsr = p.vs[1];
-  const int qw0 = q0 + wave * 32;
 
-  // Q fragments (B operand of S^T = K Q^T): row qw0 + l32, d = hi*8 + 16*kk.
-  // Rows past s_q are zero; a negative scale is folded in by negating Q, a zero
-  // scale by zeroing it.
+  // Q fragments (B operand of S^T = K Q^T): this lane's row, d = hi*8 + 16*kk.
+  // Rows past the end are zero; a negative scale is folded in by negating Q, a
+  // zero scale by zeroing it.
   u32x4_t qf[RB][KK];
   {
-    const int i = qw0 + l32;
+    const unsigned short* __restrict__ Qr =
+        (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)my_i * p.qs[1] + (int64_t)my_h * p.qs[2];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4_t x = {0u, 0u, 0u, 0u};
-      if (i < p.s_q && !p.zero_q) {
-        x = *(const u32x4_t*)(Qg + (int64_t)i * p.qs[1] + hi * 8 + kk * 16);
+      if (row_ok && !p.zero_q) {
+        x = *(const u32x4_t*)(Qr + hi * 8 + kk * 16);
         if (p.neg_q) x ^= 0x80008000u;
       }
       qf[0][kk] = x;
@@ -252,7 +268,7 @@ void fwdp_kernel(const FwdParams p) {
 
   // -inf for keys past the range end and (causal) keys after a row's diagonal.
   auto mask_tile = [&](f32x16_t (&s)[NB][RB], int k0) {
-    const int i = qw0 + l32;
+    const int i = my_i;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = k0 + (r / 4) * 8 + hi * 4 + (r % 4);
@@ -319,7 +335,7 @@ void fwdp_kernel(const FwdParams p) {
   else __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  if (T > 0) {
+  if (T > 0 && live) {
     u32x4_t kf[KK][NB];
     read_k(kbuf[0], kf);
     qk(kf, sA);
@@ -348,20 +364,22 @@ void fwdp_kernel(const FwdParams p) {
     if (hc == 2 || t + P - 1 < T) stage(Vg, vsr, voff, true, t + P - 1, vb_w, hc == 2);
     const bool has_next = hc >= 1 || t + 1 < T;
     const int k0 = k_lo + t * BN;
-    const bool need_mask = hc != 2 && ((k0 + BN > k_hi) || (CAUSAL && k0 + BN - 1 > qw0 + off));
-    u32x4_t kf[KK][NB], vf[CB][NT16];
-    if (!first) read_v(vb_r, vf);
-    if (need_mask) mask_tile(s, k0);
-    __builtin_amdgcn_sched_barrier(0);
-    float ls[RB];
-    if (!first) pv(vf, p_prev);
-    if (has_next) read_k(kb_r, kf);
-    expo(s, p_cur, ls);
-    if (has_next) qk(kf, s_next);
-    __builtin_amdgcn_sched_barrier(0);
-    const bool bad = m[0] == -INFINITY || !(ls[0] <= PMAX);
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) rebase(s, p_cur, ls);
-    l[0] += ls[0];
+    const bool need_mask = hc != 2 && ((k0 + BN > k_hi) || (CAUSAL && k0 + BN - 1 > pos_wave_lo + off));
+    if (live) {
+      u32x4_t kf[KK][NB], vf[CB][NT16];
+      if (!first) read_v(vb_r, vf);
+      if (need_mask) mask_tile(s, k0);
+      __builtin_amdgcn_sched_barrier(0);
+      float ls[RB];
+      if (!first) pv(vf, p_prev);
+      if (has_next) read_k(kb_r, kf);
+      expo(s, p_cur, ls);
+      if (has_next) qk(kf, s_next);
+      __builtin_amdgcn_sched_barrier(0);
+      const bool bad = m[0] == -INFINITY || !(ls[0] <= PMAX);
+      if (__builtin_amdgcn_ballot_w64(bad) != 0) rebase(s, p_cur, ls);
+      l[0] += ls[0];
+    }
     asm volatile("" ::: "memory");
     if (hc == 2 || t + P + 1 < T) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0((P - 1) * PAIR));
     else __builtin_amdgcn_s_waitcnt(0);
@@ -385,7 +403,7 @@ void fwdp_kernel(const FwdParams p) {
   // last (up to NBUF) steps, which know nothing at compile time.
   const int n_full = (k_hi - k_lo) / BN;
   int t_clean = n_full - P - 1;
-  if (CAUSAL) t_clean = min(t_clean, (q0 + off - k_lo + 1) / BN);
+  if (CAUSAL) t_clean = min(t_clean, (pos_wg_lo + off - k_lo + 1) / BN);
   if (T > 0) iter(IC<0>{}, 0, true, sA, sB, pB, pA, kbuf[0], kbuf[1], vbuf[NBUF - 2], vbuf[NBUF - 1]);
   int t = 1;
   for (; t + NBUF <= t_clean; t += NBUF) {
@@ -410,7 +428,7 @@ void fwdp_kernel(const FwdParams p) {
     if (t + 2 < T) step(IC<0>{}, t + 2, IC<3>{});
     if (t + 3 < T) step(IC<0>{}, t + 3, IC<0>{});
   }
-  if (T >= 1) {
+  if (T >= 1 && live) {
     u32x4_t vf[CB][NT16];
     read_v(vbuf[(T - 1) % NBUF], vf);
     if ((T - 1) & 1) pv(vf, pB);
@@ -419,12 +437,12 @@ void fwdp_kernel(const FwdParams p) {
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
   {
-    const int i = qw0 + l32;
+    const int i = my_i, hh = my_h;
     const float lt = pair_sum(l[0]);
     const bool has = lt > 0.f;
     const float inv = has ? 1.f / lt : 0.f;
     const float lse = has ? (m[0] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
-    if (i < p.s_q) {
+    if (row_ok) {
       if (SPLIT) {
         const int64_t rowi = (((int64_t)split * p.b + bb) * p.h + hh) * p.s_q + i;
         float* op = p.o_part + rowi * D;
@@ -460,21 +478,28 @@ void fwdp_kernel(const FwdParams p) {
 // ---------------------------------------------------------------------------
 // Launchers
 
-template <int T_, int D, int BN, int NW, int NBUF, bool CAUSAL, bool SPLIT>
+template <int T_, int D, int BN, int NW, int NBUF, bool PACK, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwdp_t(const FwdParams& p, hipStream_t st) {
   constexpr int BM = NW * 32;
   FwdParams q = p;
-  q.n_qt = (p.s_q + BM - 1) / BM;
-  const int64_t grid = (int64_t)q.n_qt * p.b * p.h * p.n_splits;
-  hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, NW, NBUF, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
+  const int64_t rows = PACK ? (int64_t)p.g * p.s_q : p.s_q;
+  const int64_t nh = PACK ? p.h / p.g : p.h;
+  q.n_qt = (int)((rows + BM - 1) / BM);
+  const int64_t grid = (int64_t)q.n_qt * p.b * nh * p.n_splits;
+  hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, NW, NBUF, PACK, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
   return hipGetLastError();
 }
 
 template <int T_, int D, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwd_d(const FwdParams& p, hipStream_t st) {
   // d <= 32: 4 waves (128 query rows) per work-group and up to four waves per SIMD
-  if constexpr (D >= 64) return launch_fwdp_t<T_, D, kPrefillBN, kPrefillNW, kPrefillNBUF, CAUSAL, SPLIT>(p, st);
-  else return launch_fwdp_t<T_, D, kPrefillBN, 4, kPrefillNBUF, CAUSAL, SPLIT>(p, st);
+  if constexpr (D >= 64) {
+    if (fwd_packed(p.g, p.s_q, D))
+      return launch_fwdp_t<T_, D, kPrefillBN, kPrefillNW, kPrefillNBUF, true, CAUSAL, SPLIT>(p, st);
+    return launch_fwdp_t<T_, D, kPrefillBN, kPrefillNW, kPrefillNBUF, false, CAUSAL, SPLIT>(p, st);
+  } else {
+    return launch_fwdp_t<T_, D, kPrefillBN, 4, kPrefillNBUF, false, CAUSAL, SPLIT>(p, st);
+  }
 }
 
 template <int T_, bool CAUSAL, bool SPLIT>

@@ -69,11 +69,16 @@ constexpr int kDecodeBatch = ATTN_DECODE_BATCH;
 inline int fwd_rows_per_block(int d, int s_q) {
   return s_q == 1 ? 1 : (d >= 64 ? kPrefillNW * 32 : 4 * 32);
 }
-// Work-groups per split: the decode kernel (s_q == 1) puts kDecodeHeads heads in
-// one work-group; the prefill kernel one (b, h, query row block) per work-group.
-inline int64_t fwd_groups_per_split(int64_t b, int64_t h, int64_t s_q, int d) {
+// Query heads sharing a K/V head (g > 1) with few query rows: the prefill kernel
+// packs a K/V head's g * s_q query rows into its work-groups (d >= 64).
+inline bool fwd_packed(int64_t g, int64_t s_q, int d) { return g > 1 && s_q <= 64 && d >= 64; }
+// Work-groups per split: packed, one per (b, K/V head, block of packed rows);
+// the decode kernel (s_q == 1) puts kDecodeHeads heads in one work-group; the
+// prefill kernel one (b, h, query row block) per work-group.
+inline int64_t fwd_groups_per_split(int64_t b, int64_t h, int64_t g, int64_t s_q, int d) {
+  const int64_t bm = d >= 64 ? kPrefillNW * 32 : 4 * 32;  // prefill rows per work-group
+  if (fwd_packed(g, s_q, d)) return b * (h / g) * ((g * s_q + bm - 1) / bm);
   if (s_q == 1) return (b * h + kDecodeHeads - 1) / kDecodeHeads;
-  const int64_t bm = fwd_rows_per_block(d, (int)s_q);
   return b * h * ((s_q + bm - 1) / bm);
 }
 
@@ -81,10 +86,13 @@ inline int64_t fwd_groups_per_split(int64_t b, int64_t h, int64_t s_q, int d) {
 hipError_t launch_prefill(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st);
 // One-row decode kernel (s_q == 1).
 hipError_t launch_decode(const FwdParams& p, int dtype, bool split, hipStream_t st);
-// One of the two above, by s_q.  With one query row the bottom-right causal mask
-// hides nothing, so the causal flag does not matter there.
+// One of the two above: the decode kernel for one query row unless query heads
+// share K/V heads (then the packed prefill kernel reads each K/V tile once per
+// group).  With one query row the bottom-right causal mask hides nothing, so the
+// causal flag does not matter there.
 inline hipError_t launch_fwd(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st) {
-  return p.s_q == 1 ? launch_decode(p, dtype, split, st) : launch_prefill(p, dtype, causal, split, st);
+  return p.s_q == 1 && !fwd_packed(p.g, p.s_q, p.d) ? launch_decode(p, dtype, split, st)
+                                                     : launch_prefill(p, dtype, causal, split, st);
 }
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t st);
 

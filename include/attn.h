@@ -127,6 +127,17 @@ attn_status attn_num_splits(int64_t b, int64_t h, int64_t s_q, int64_t s_k, int6
 attn_status attn_num_splits_for(int64_t b, int64_t h, int64_t s_q, int64_t s_k,
                                 int64_t d, int32_t num_cus, int32_t *n_out);
 
+/* The heuristic for query heads sharing K/V heads (h_kv as in attn_args; 0 or h
+ * gives the two functions above).  With h_kv < h, s_q <= 64 and d >= 64 the
+ * library packs the g = h / h_kv query heads of a K/V head, and their s_q rows,
+ * into the same work-groups (each K/V tile then serves the whole group), so a
+ * split has b * h_kv * ceil(g * s_q / 256) work-groups.  Errors as above, plus
+ * ATTN_E_SHAPE for an h_kv that attn_args would reject. */
+attn_status attn_num_splits_kv(int64_t b, int64_t h, int64_t h_kv, int64_t s_q, int64_t s_k,
+                               int64_t d, int device, int32_t *n_out);
+attn_status attn_num_splits_kv_for(int64_t b, int64_t h, int64_t h_kv, int64_t s_q, int64_t s_k,
+                                   int64_t d, int32_t num_cus, int32_t *n_out);
+
 /* First stage of flash-decoding (issue #1248): per split i, the attention of
  * every query over the keys of split i only.  Writes
  *   o_part  : dense fp32 [num_splits, b, h, s_q, d], O_i normalised within split i

@@ -234,6 +234,42 @@ def test_shared_kv_heads(case):
     check(O2, L2, O_ref, L_ref, dt, f"{case} split")
 
 
+PACKED_CASES = [
+    # dtype, b, s_q, s_k, h, h_kv, d, causal, splits: few query rows per head with
+    # h / h_kv > 1 (d >= 64), so one work-group takes all query heads of a K/V
+    # head; packed rows span work-groups and heads, with ragged ends
+    ("bf16", 2, 64, 1000, 16, 2, 128, True, 5),    # 512 packed rows: 2 blocks per K/V head
+    ("fp16", 1, 37, 700, 14, 2, 128, False, 3),    # 259 rows: a 3-row second block
+    ("bf16", 3, 40, 30, 4, 1, 64, True, 2),        # s_q > s_k: causal rows that see no key
+    ("fp16", 2, 1, 2049, 32, 4, 64, False, 7),     # one row per head, 8 heads per K/V head
+    ("bf16", 1, 5, 333, 12, 3, 128, True, 1),
+    ("fp16", 2, 9, 64, 6, 2, 128, True, 64),       # one key per split
+]
+
+
+@pytest.mark.parametrize("case", PACKED_CASES, ids=[f"{c[0]}-b{c[1]}-q{c[2]}-k{c[3]}-h{c[4]}-kv{c[5]}-d{c[6]}-n{c[8]}" for c in PACKED_CASES])
+def test_packed_query_heads(case):
+    dt, b, s_q, s_k, h, h_kv, d, causal, n = case
+    say("attn_fwd packed query heads", case)
+    q, k, v = workloads.make_qkv(b, s_q, s_k, h, d, dt, seed=23, h_kv=h_kv)
+    scale = 1 / math.sqrt(d)
+    O_ref, L_ref = oracle.attention(*host64(q, k, v), scale, causal)
+    O, L = run_fwd(q, k, v, scale, causal)
+    check(O, L, O_ref, L_ref, dt, f"{case} fused")
+    qd, kd, vd = upload(q, k, v)
+    Op, Lp = ea.attn_fwd_splitkv(qd, kd, vd, num_splits=n, softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    Op_ref, Lp_ref = oracle.attention_split(*host64(q, k, v), scale, causal, oracle.split_bounds(s_k, n))
+    Lp_h = f64(Lp)
+    fin = np.isfinite(Lp_ref)
+    assert np.array_equal(np.isfinite(Lp_h), fin)
+    assert np.abs(Lp_h[fin] - Lp_ref[fin]).max() <= TOL_LSE
+    assert np.abs(f64(Op) - Op_ref).max() <= TOL_O[dt]
+    O2, L2 = ea.attn_combine(Op, Lp, q.dtype)
+    torch.cuda.synchronize()
+    check(O2, L2, O_ref, L_ref, dt, f"{case} split")
+
+
 @pytest.mark.parametrize("s_q", [1, 4, 10])
 def test_multi_token_decode_48_heads(s_q):
     # issue #1248's decode setting: batch 8, 48 query heads, 1-10 new tokens
