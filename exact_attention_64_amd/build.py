@@ -16,7 +16,13 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libattn.so")
 
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_decode.hip", "attn_combine.hip"]
+# (source, object name, extra flags).  The prefill kernels are compiled once per
+# (input type, causal) pair so that the four sets build in parallel.
+SOURCES = [("attn_api.cpp", "attn_api", []),
+           *[("attn_fwd.hip", f"attn_fwd_t{t}_c{c}", [f"-DATTN_FWD_DTYPE={t}", f"-DATTN_FWD_CAUSAL={c}"])
+             for t in (0, 1) for c in (0, 1)],
+           ("attn_decode.hip", "attn_decode", []),
+           ("attn_combine.hip", "attn_combine", [])]
 
 # Packed fp32 VALU instructions are switched off for every HIP translation unit.
 # MFMA accumulators are kept in VGPRs (the prefill kernel's vector ALU works on
@@ -40,16 +46,16 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
     objs = []
     procs = []
-    for src in SOURCES:
-        obj = os.path.join(HERE, "_build", src + ".o")
+    for src, name, extra in SOURCES:
+        obj = os.path.join(HERE, "_build", name + ".o")
         os.makedirs(os.path.dirname(obj), exist_ok=True)
-        cmd = [cc, *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIP_FLAGS, *extra, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd.insert(1, "-x")
             cmd.insert(2, "hip")
         if verbose:
             print(" ".join(cmd), flush=True)
-        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        procs.append((name, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         objs.append(obj)
     failed = []
     for src, pr in procs:

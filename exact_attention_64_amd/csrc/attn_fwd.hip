@@ -76,19 +76,31 @@ template <int N> struct IC { static constexpr int value = N; };
 // per-wave offset); the kernel orders these loads with its own s_waitcnt
 // vmcnt and barriers.  Loads complete in order, so the compiler's own vmcnt
 // waits for other loads stay correct.  The s_nop covers the M0 -> LDS DMA
-// hazard.
+// hazard.  NT sets the nontemporal bit: a tile that no other work-group reads
+// should not allocate in the caches, where it would only push other lines out
+// (dirty ones at the cost of a write-back each; measured on gfx950, default-
+// policy streaming reads fall to about half the rate of nontemporal ones when
+// the last-level cache holds dirty lines, and run about 12% slower when clean).
+template <bool NT>
 __device__ __forceinline__ void lds_dma16(const void* gptr, const char* lds) {
   const unsigned m0v = (unsigned)(uintptr_t)(const LDS_AS char*)lds;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(m0v), "v"(gptr)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 :
+                 : "s"(m0v), "v"(gptr)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(m0v), "v"(gptr)
+                 : "memory", "m0");
 }
 
 // PACK (query heads sharing a K/V head, few query rows): a work-group covers one
 // (batch, K/V head) and its g * s_q query rows, row r being query head
 // hk * g + r / s_q at position r % s_q, so every K/V tile serves the whole group.
-template <int T_, int D, int BN, int NW, int NBUF, bool PACK, bool CAUSAL, bool SPLIT>
+// NT: K/V tiles are read with the nontemporal bit (few work-groups read each tile).
+template <int T_, int D, int BN, int NW, int NBUF, bool PACK, bool NT, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 64 ? 2 : 4, D >= 64 ? 2 : 4)))
 void fwdp_kernel(const FwdParams p) {
   using Tt = Ty<T_>;
@@ -209,7 +221,7 @@ void fwdp_kernel(const FwdParams p) {
       const unsigned short* __restrict__ Gt = G + (int64_t)k0 * gs;
 #pragma unroll
       for (int i = 0; i < WL; ++i)
-        lds_dma16((const void*)(Gt + goff[i]), buf + (wave * WL + i) * 1024);
+        lds_dma16<NT>((const void*)(Gt + goff[i]), buf + (wave * WL + i) * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < WL; ++i) {
@@ -217,7 +229,7 @@ void fwdp_kernel(const FwdParams p) {
         const int row = slot / NCH, pc = slot % NCH;
         const int key = min(k0 + row, k_hi - 1);
         const int ch = pc ^ (isv ? Swz<D>::v(row) : Swz<D>::k(row));
-        lds_dma16((const void*)(G + (int64_t)key * gs + ch * 8), buf + (wave * WL + i) * 1024);
+        lds_dma16<NT>((const void*)(G + (int64_t)key * gs + ch * 8), buf + (wave * WL + i) * 1024);
       }
     }
   };
@@ -486,7 +498,17 @@ static hipError_t launch_fwdp_t(const FwdParams& p, hipStream_t st) {
   const int64_t nh = PACK ? p.h / p.g : p.h;
   q.n_qt = (int)((rows + BM - 1) / BM);
   const int64_t grid = (int64_t)q.n_qt * p.b * nh * p.n_splits;
-  hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, NW, NBUF, PACK, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
+  // Nontemporal K/V loads when at most kStreamQTiles work-groups read each tile
+  // and a key row fills whole 128-byte lines (d >= 64): shorter rows share
+  // lines with the neighbouring heads that other work-groups read, and reading
+  // them nontemporally measured slower (b = 512, s = 150, h = 16, d = 16).
+  if constexpr (D >= 64) {
+    if (q.n_qt <= kStreamQTiles) {
+      hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, NW, NBUF, PACK, true, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, NW, NBUF, PACK, false, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
   return hipGetLastError();
 }
 
@@ -512,15 +534,17 @@ static hipError_t launch_fwd_c(const FwdParams& p, hipStream_t st) {
   }
 }
 
-template <int T_>
-static hipError_t launch_fwd_dt(const FwdParams& p, bool causal, bool split, hipStream_t st) {
-  if (causal) return split ? launch_fwd_c<T_, true, true>(p, st) : launch_fwd_c<T_, true, false>(p, st);
-  return split ? launch_fwd_c<T_, false, true>(p, st) : launch_fwd_c<T_, false, false>(p, st);
+template <int T_, bool CAUSAL>
+hipError_t launch_prefill_tc(const FwdParams& p, bool split, hipStream_t st) {
+  return split ? launch_fwd_c<T_, CAUSAL, true>(p, st) : launch_fwd_c<T_, CAUSAL, false>(p, st);
 }
 
-hipError_t launch_prefill(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st) {
-  return dtype == kBF16 ? launch_fwd_dt<kBF16>(p, causal, split, st)
-                        : launch_fwd_dt<kFP16>(p, causal, split, st);
-}
+// The library compiles this file once per (input type, causal) pair, selected
+// by ATTN_FWD_DTYPE and ATTN_FWD_CAUSAL, so the four kernel sets build in
+// parallel; launch_prefill (attn_internal.h) picks among them.
+#if !defined(ATTN_FWD_DTYPE) || !defined(ATTN_FWD_CAUSAL)
+#error "compile with -DATTN_FWD_DTYPE=<0|1> -DATTN_FWD_CAUSAL=<0|1>"
+#endif
+template hipError_t launch_prefill_tc<ATTN_FWD_DTYPE, (ATTN_FWD_CAUSAL != 0)>(const FwdParams&, bool, hipStream_t);
 
 }  // namespace attn

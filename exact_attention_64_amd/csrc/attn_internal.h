@@ -51,6 +51,9 @@ struct CombineParams {
 #ifndef ATTN_PREFILL_NBUF
 #define ATTN_PREFILL_NBUF 4 // LDS ring buffers per tensor (prefetch depth + 1), 2 or 4
 #endif
+#ifndef ATTN_STREAM_QTILES
+#define ATTN_STREAM_QTILES 2 // prefill K/V loads are nontemporal when at most this many work-groups read a tile
+#endif
 #ifndef ATTN_DECODE_HEADS
 #define ATTN_DECODE_HEADS 4 // heads (one wave each) per work-group of the decode kernel
 #endif
@@ -60,6 +63,7 @@ struct CombineParams {
 constexpr int kPrefillNW = ATTN_PREFILL_NW;
 constexpr int kPrefillBN = ATTN_PREFILL_BN;
 constexpr int kPrefillNBUF = ATTN_PREFILL_NBUF;
+constexpr int kStreamQTiles = ATTN_STREAM_QTILES;
 constexpr int kDecodeHeads = ATTN_DECODE_HEADS;
 constexpr int kDecodeBatch = ATTN_DECODE_BATCH;
 
@@ -82,8 +86,18 @@ inline int64_t fwd_groups_per_split(int64_t b, int64_t h, int64_t g, int64_t s_q
   return b * h * ((s_q + bm - 1) / bm);
 }
 
-// Fused / split-KV prefill kernel (s_q >= 1; used for s_q > 1).
-hipError_t launch_prefill(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st);
+// Fused / split-KV prefill kernel (s_q >= 1; used for s_q > 1), one explicit
+// instantiation per (input type, causal) pair in its own object file.
+template <int T_, bool CAUSAL>
+hipError_t launch_prefill_tc(const FwdParams& p, bool split, hipStream_t st);
+extern template hipError_t launch_prefill_tc<kFP16, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_prefill_tc<kFP16, true>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_prefill_tc<kBF16, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_prefill_tc<kBF16, true>(const FwdParams&, bool, hipStream_t);
+inline hipError_t launch_prefill(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st) {
+  if (dtype == kBF16) return causal ? launch_prefill_tc<kBF16, true>(p, split, st) : launch_prefill_tc<kBF16, false>(p, split, st);
+  return causal ? launch_prefill_tc<kFP16, true>(p, split, st) : launch_prefill_tc<kFP16, false>(p, split, st);
+}
 // One-row decode kernel (s_q == 1).
 hipError_t launch_decode(const FwdParams& p, int dtype, bool split, hipStream_t st);
 // One of the two above: the decode kernel for one query row unless query heads
