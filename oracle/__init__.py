@@ -5,12 +5,14 @@ anything here. The GPU library never calls it and shares no code with it.
 
 * ``oracle.exact``: the plain float64 definition (score matrix materialised,
   max-subtracted softmax, product with V, per-row log-sum-exp), the per-split
-  form and the split reduction.
+  form, the split reduction, and both over a paged K/V cache.
 * ``oracle.brute``: the same definition as scalar Python loops with ``math.fsum``,
   for tiny shapes only.
 """
 from .exact import (attention, attention_rows, attention_split, combine,
-                        softmax_rows, visible_mask, split_bounds)
+                        softmax_rows, visible_mask, split_bounds, gather_paged,
+                        attention_paged, attention_split_paged)
 
 __all__ = ["attention", "attention_rows", "attention_split", "combine",
-           "softmax_rows", "visible_mask", "split_bounds"]
+           "softmax_rows", "visible_mask", "split_bounds", "gather_paged",
+           "attention_paged", "attention_split_paged"]

@@ -31,6 +31,15 @@ h_kv; O is (b, s_q, h, d); LSE is (b, h, s_q).  Query head hh attends with K/V
 head hh // (h / h_kv): h_kv = h is plain multi-head attention, and a smaller
 h_kv lets consecutive query heads share one K/V head (the several "q heads" over
 one K tile asked about in issue #1248).
+
+Paged K/V cache ("LLM Lab Notes 07", §5 "Engineering Takeaways", names the paged
+KV cache as the standard companion of the fused kernel for long contexts and
+gives no layout; the plainest reading is taken): the cache is an array of
+fixed-size blocks, (num_blocks, block_size, h_kv, d); sequence bi has
+seqlens_k[bi] keys, key j of it living in physical block block_table[bi, j //
+block_size] at slot j % block_size.  Gathering a sequence's keys in order gives
+the contiguous K of the definition above, and each sequence is attended over
+its own key count (the causal rule uses that count as s_k).
 """
 from __future__ import annotations
 
@@ -190,3 +199,54 @@ def combine(o_parts, lse_parts):
     scale = np.where(finite[None], scale, 0.0)
     O = (scale[..., None] * o_parts).sum(axis=0)
     return O, lse
+
+
+def gather_paged(cache, table_row, length: int, block_size: int):
+    """Keys 0..length-1 of one sequence from a paged cache, in order: key j is
+    slot j % block_size of physical block table_row[j // block_size].
+    cache (num_blocks, block_size, h_kv, d) -> (length, h_kv, d)."""
+    j = np.arange(int(length))
+    return np.asarray(cache)[np.asarray(table_row, dtype=np.int64)[j // block_size], j % block_size]
+
+
+def attention_paged(q, k_cache, v_cache, block_table, seqlens_k, scale: float, causal: bool):
+    """Exact attention over a paged K/V cache with a key count per sequence.
+
+    Sequence bi attends over its seqlens_k[bi] keys gathered by ``gather_paged``,
+    through ``attention`` (so the causal rule is j <= i + seqlens_k[bi] - s_q and a
+    sequence with no visible key gets O = 0, LSE = -inf). Returns
+    (O (b,s_q,h,d), LSE (b,h,s_q)), float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    b, s_q, h, d = q.shape
+    bs = np.asarray(k_cache).shape[1]
+    O = np.zeros((b, s_q, h, d))
+    LSE = np.zeros((b, h, s_q))
+    for bi in range(b):
+        n = int(seqlens_k[bi])
+        k = gather_paged(k_cache, block_table[bi], n, bs)[None]
+        v = gather_paged(v_cache, block_table[bi], n, bs)[None]
+        o, lse = attention(q[bi:bi + 1], k, v, scale, causal)
+        O[bi] = o[0]
+        LSE[bi] = lse[0]
+    return O, LSE
+
+
+def attention_split_paged(q, k_cache, v_cache, block_table, seqlens_k, scale: float,
+                          causal: bool, n: int):
+    """Per-split partials over a paged cache: split i of sequence bi covers that
+    sequence's keys split_bounds(seqlens_k[bi], n)[i]. Returns O_parts
+    (n, b, h, s_q, d) and LSE_parts (n, b, h, s_q), as ``attention_split``."""
+    q = np.asarray(q, dtype=np.float64)
+    b, s_q, h, d = q.shape
+    bs = np.asarray(k_cache).shape[1]
+    O = np.zeros((n, b, h, s_q, d))
+    LSE = np.zeros((n, b, h, s_q))
+    for bi in range(b):
+        sk = int(seqlens_k[bi])
+        k = gather_paged(k_cache, block_table[bi], sk, bs)[None]
+        v = gather_paged(v_cache, block_table[bi], sk, bs)[None]
+        o, lse = attention_split(q[bi:bi + 1], k, v, scale, causal, split_bounds(sk, n))
+        O[:, bi] = o[:, 0]
+        LSE[:, bi] = lse[:, 0]
+    return O, LSE

@@ -282,10 +282,106 @@ def pin_gqa_brute():
         np.testing.assert_allclose(L, np.array(Lb), atol=1e-12)
 
 
+def _paged_from_contiguous(k, block_size):
+    """(b, s_k, h_kv, d) with s_k a multiple of block_size -> cache of b * s_k /
+    block_size blocks in sequence order, and the identity block table."""
+    b, s_k = k.shape[:2]
+    nb = s_k // block_size
+    cache = k.reshape(b * nb, block_size, *k.shape[2:])
+    return cache, np.arange(b * nb).reshape(b, nb)
+
+
+def pin_paged_identity_table():
+    # blocks laid out in sequence order with the identity table and full lengths:
+    # the plain definition on the contiguous tensors, full and split forms
+    r = np.random.default_rng(41)
+    b, s_q, s_k, h, h_kv, d, bs = 2, 5, 24, 4, 2, 3, 8
+    q = r.standard_normal((b, s_q, h, d))
+    k = r.standard_normal((b, s_k, h_kv, d))
+    v = r.standard_normal((b, s_k, h_kv, d))
+    kc, table = _paged_from_contiguous(k, bs)
+    vc, _ = _paged_from_contiguous(v, bs)
+    lens = [s_k] * b
+    for causal in (False, True):
+        O, L = oracle.attention(q, k, v, 0.7, causal)
+        Op, Lp = oracle.attention_paged(q, kc, vc, table, lens, 0.7, causal)
+        np.testing.assert_allclose(Op, O, atol=1e-14)
+        np.testing.assert_allclose(Lp, L, atol=1e-14)
+        Os, Ls = oracle.attention_split(q, k, v, 0.7, causal, oracle.split_bounds(s_k, 3))
+        Osp, Lsp = oracle.attention_split_paged(q, kc, vc, table, lens, 0.7, causal, 3)
+        np.testing.assert_allclose(Osp, Os, atol=1e-14)
+        np.testing.assert_allclose(Lsp, Ls, atol=1e-14)
+
+
+def pin_paged_block_permutation():
+    # moving the physical blocks and rewriting the table to follow them changes nothing
+    r = np.random.default_rng(43)
+    b, s_q, s_k, h, d, bs = 3, 4, 20, 2, 3, 4
+    q = r.standard_normal((b, s_q, h, d))
+    k = r.standard_normal((b, s_k, h, d))
+    v = r.standard_normal((b, s_k, h, d))
+    kc, table = _paged_from_contiguous(k, bs)
+    vc, _ = _paged_from_contiguous(v, bs)
+    perm = r.permutation(kc.shape[0])       # block i moves to slot perm[i]
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[perm], vc2[perm] = kc, vc
+    lens = [20, 13, 6]
+    for causal in (False, True):
+        O, L = oracle.attention_paged(q, kc, vc, table, lens, 0.9, causal)
+        O2, L2 = oracle.attention_paged(q, kc2, vc2, perm[table], lens, 0.9, causal)
+        np.testing.assert_allclose(O2, O, atol=1e-14)
+        np.testing.assert_allclose(L2, L, atol=1e-14)
+
+
+def pin_paged_lengths_brute():
+    # per-sequence key counts (one empty, one ending mid-block) on a scattered
+    # table, against the scalar brute force on keys fetched one by one: key j of
+    # sequence bi is slot j % bs of block table[bi][j // bs]
+    r = np.random.default_rng(47)
+    b, s_q, h, h_kv, d, bs = 3, 3, 2, 1, 4, 4
+    lens = [5, 0, 11]
+    nblk = 10
+    kc = r.standard_normal((nblk, bs, h_kv, d))
+    vc = r.standard_normal((nblk, bs, h_kv, d))
+    table = [[7, 2, 9], [4, 0, 1], [3, 8, 5]]
+    q = r.standard_normal((b, s_q, h, d))
+    for causal in (False, True):
+        O, L = oracle.attention_paged(q, kc, vc, np.array(table), lens, 0.5, causal)
+        for bi in range(b):
+            if lens[bi] == 0:  # no key at all: O = 0, LSE = -inf
+                assert np.all(O[bi] == 0) and np.all(L[bi] == -np.inf)
+                continue
+            ks = [[[float(x) for x in kc[table[bi][j // bs]][j % bs][hk]] for hk in range(h_kv)]
+                  for j in range(lens[bi])]
+            vs = [[[float(x) for x in vc[table[bi][j // bs]][j % bs][hk]] for hk in range(h_kv)]
+                  for j in range(lens[bi])]
+            Ob, Lb = attention_brute(q[bi:bi + 1], [ks], [vs], 0.5, causal)
+            np.testing.assert_allclose(O[bi], np.array(Ob)[0], atol=1e-12)
+            np.testing.assert_allclose(L[bi], np.array(Lb)[0], atol=1e-12)
+
+
+def pin_paged_split_combines():
+    # splits over each sequence's own key count (some splits empty) combine to the whole
+    r = np.random.default_rng(53)
+    b, s_q, h, d, bs = 3, 6, 2, 5, 8
+    lens = [2, 0, 30]
+    kc = r.standard_normal((12, bs, h, d))
+    vc = r.standard_normal((12, bs, h, d))
+    table = r.permutation(12)[:12].reshape(3, 4)
+    q = r.standard_normal((b, s_q, h, d))
+    for causal in (False, True):
+        O, L = oracle.attention_paged(q, kc, vc, table, lens, 0.4, causal)
+        Op, Lp = oracle.attention_split_paged(q, kc, vc, table, lens, 0.4, causal, 4)
+        Oc, Lc = oracle.combine(Op, Lp)
+        np.testing.assert_allclose(Oc.transpose(0, 2, 1, 3), O, atol=1e-13)
+        np.testing.assert_allclose(Lc, L, atol=1e-13)
+
+
 PINS = [pin_golden, pin_brute, pin_torch_special_case, pin_rows_sum_to_one, pin_constant_v,
         pin_q_zero_closed_form, pin_single_key, pin_key_shift, pin_key_permutation,
         pin_split_equals_unsplit, pin_identical_splits, pin_rows_subset,
-        pin_gqa_is_mha_on_repeated_heads, pin_gqa_brute]
+        pin_gqa_is_mha_on_repeated_heads, pin_gqa_brute, pin_paged_identity_table,
+        pin_paged_block_permutation, pin_paged_lengths_brute, pin_paged_split_combines]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -363,8 +459,27 @@ def _kv_head_modulo(h, h_kv):
     return np.arange(h) % h_kv
 
 
+def _gather_table_ignored(cache, table_row, length, block_size):
+    j = np.arange(int(length))
+    return np.asarray(cache)[j // block_size, j % block_size]
+
+
+def _gather_whole_blocks(cache, table_row, length, block_size):
+    nb = -(-int(length) // block_size)
+    j = np.arange(nb * block_size)
+    return np.asarray(cache)[np.asarray(table_row)[j // block_size], j % block_size]
+
+
+def _gather_slot_from_end(cache, table_row, length, block_size):
+    j = np.arange(int(length))
+    return np.asarray(cache)[np.asarray(table_row)[j // block_size], block_size - 1 - j % block_size]
+
+
 MUTANTS = {
     "gqa_head_modulo": ("kv_head_of", _kv_head_modulo),
+    "paged_table_ignored": ("gather_paged", _gather_table_ignored),
+    "paged_whole_blocks": ("gather_paged", _gather_whole_blocks),
+    "paged_slot_reversed": ("gather_paged", _gather_slot_from_end),
     "softmax_no_max": ("softmax_rows", _softmax_no_max),
     "lse_without_max": ("softmax_rows", _softmax_lse_without_max),
     "causal_top_left": ("visible_mask", _mask_top_left),
@@ -395,6 +510,20 @@ def test_mutant_is_caught(name, monkeypatch):
 
 
 # ------------------------------------------------------ input recipe ----
+
+def test_paged_inputs_are_seeded_and_scattered():
+    a = workloads.make_paged(3, 2, 4, 16, "bf16", [70, 0, 33], 32, h_kv=2, seed=5)
+    b = workloads.make_paged(3, 2, 4, 16, "bf16", [70, 0, 33], 32, h_kv=2, seed=5)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    q, kc, vc, table, lens = a
+    assert q.shape == (3, 2, 4, 16) and kc.shape == vc.shape == (3 * 3 + 3, 32, 2, 16)
+    assert table.shape == (3, 3) and table.dtype == torch.int32
+    ids = table.flatten().tolist()
+    assert len(set(ids)) == len(ids) and min(ids) >= 0 and max(ids) < kc.shape[0]
+    assert ids != sorted(ids)
+    assert lens.tolist() == [70, 0, 33] and lens.dtype == torch.int32
+
 
 def test_inputs_are_seeded_and_rounded():
     q1, k1, v1 = workloads.make_qkv(2, 5, 7, 3, 16, "bf16", seed=42)

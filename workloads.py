@@ -88,6 +88,34 @@ def make_qkv(b: int, s_q: int, s_k: int, h: int, d: int, dtype: str, seed: int =
     return q, k, v
 
 
+def make_paged(b: int, s_q: int, h: int, d: int, dtype: str, seqlens, block_size: int,
+               h_kv: int = 0, seed: int = 42, spare_blocks: int = 3):
+    """Draw a query and a paged K/V cache for per-sequence key counts ``seqlens``.
+
+    * q (b, s_q, h, d), then k_cache and v_cache (num_blocks, block_size, h_kv, d),
+      each i.i.d. N(0, 1) from one CPU generator seeded with ``seed``, rounded to
+      ``dtype``;
+    * block_table (b, max_blocks) int32: a seeded random permutation of the
+      physical blocks, so each sequence owns distinct, scattered blocks; with
+      max_blocks = ceil(max(seqlens) / block_size) (at least 1), num_blocks =
+      b * max_blocks + spare_blocks, and the spare blocks belong to no sequence;
+    * seqlens (b,) int32 as given.
+
+    Returns CPU tensors (q, k_cache, v_cache, block_table, seqlens).
+    """
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    td = DTYPES[dtype]
+    hk = h_kv or h
+    max_blocks = max(1, -(-max(seqlens) // block_size))
+    num_blocks = b * max_blocks + spare_blocks
+    q = torch.randn((b, s_q, h, d), generator=g, dtype=torch.float32).to(td)
+    k_cache = torch.randn((num_blocks, block_size, hk, d), generator=g, dtype=torch.float32).to(td)
+    v_cache = torch.randn((num_blocks, block_size, hk, d), generator=g, dtype=torch.float32).to(td)
+    perm = torch.randperm(num_blocks, generator=g)[: b * max_blocks]
+    block_table = perm.reshape(b, max_blocks).to(torch.int32).contiguous()
+    return q, k_cache, v_cache, block_table, torch.tensor(list(seqlens), dtype=torch.int32)
+
+
 def make_workload(w: Workload, seed: int = 42):
     return make_qkv(w.b, w.s_q, w.s_k, w.h, w.d, w.dtype, seed)
 
