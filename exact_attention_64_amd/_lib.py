@@ -31,7 +31,8 @@ I64x3 = ctypes.c_int64 * 3
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_num_splits", "attn_num_splits_for", "attn_num_splits_kv",
-           "attn_num_splits_kv_for", "attn_fwd_splitkv", "attn_combine", "attn_status_str")
+           "attn_num_splits_kv_for", "attn_fwd_splitkv", "attn_combine", "attn_fwd_paged",
+           "attn_fwd_splitkv_paged", "attn_num_splits_paged", "attn_status_str")
 
 
 class AttnArgs(ctypes.Structure):
@@ -46,6 +47,24 @@ class AttnArgs(ctypes.Structure):
         ("q_stride", I64x3), ("k_stride", I64x3), ("v_stride", I64x3), ("o_stride", I64x3),
         ("softmax_scale", ctypes.c_float),
         ("h_kv", ctypes.c_int64),
+    ]
+
+
+class AttnPagedArgs(ctypes.Structure):
+    """Mirror of ``attn_paged_args`` in include/attn.h."""
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("b", ctypes.c_int64), ("s_q", ctypes.c_int64), ("h", ctypes.c_int64),
+        ("h_kv", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("q_stride", I64x3),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("k_stride", I64x3), ("v_stride", I64x3),
+        ("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int64),
+        ("max_blocks", ctypes.c_int64),
+        ("seqlens_k", ctypes.c_void_p), ("max_seqlen_k", ctypes.c_int64),
+        ("o", ctypes.c_void_p), ("o_stride", I64x3), ("lse", ctypes.c_void_p),
+        ("softmax_scale", ctypes.c_float),
     ]
 
 
@@ -90,6 +109,13 @@ def lib():
                                        ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_void_p,
                                        ctypes.c_void_p]
             L.attn_combine.restype = ctypes.c_int32
+            L.attn_fwd_paged.argtypes = [P(AttnPagedArgs), ctypes.c_void_p]
+            L.attn_fwd_paged.restype = ctypes.c_int32
+            L.attn_fwd_splitkv_paged.argtypes = [P(AttnPagedArgs), ctypes.c_int32, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+            L.attn_fwd_splitkv_paged.restype = ctypes.c_int32
+            L.attn_num_splits_paged.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, P(ctypes.c_int32)]
+            L.attn_num_splits_paged.restype = ctypes.c_int32
             L.attn_status_str.argtypes = [ctypes.c_int32]
             L.attn_status_str.restype = ctypes.c_char_p
             _lib = L
@@ -222,4 +248,104 @@ def attn_combine(o_part, lse_part, dtype=torch.bfloat16, out=None, lse=None, str
 def attn_decode(q, k, v, num_splits=0, softmax_scale=None, causal=False, stream=None):
     """Split-KV forward followed by the combine: flash-decoding end to end."""
     o_part, lse_part = attn_fwd_splitkv(q, k, v, num_splits, softmax_scale, causal, stream=stream)
+    return attn_combine(o_part, lse_part, q.dtype, stream=stream)
+
+
+# ------------------------------------------------------------ paged cache ----
+
+def make_paged_args(q, k_cache, v_cache, block_table, seqlens_k, max_seqlen_k=None,
+                    softmax_scale=None, causal=False, out=None, lse=None) -> AttnPagedArgs:
+    """Fill ``attn_paged_args`` (no copies).
+
+    q (b, s_q, h, d); k_cache, v_cache (num_blocks, block_size, h_kv, d) with a
+    contiguous last dimension; block_table int32 (b, max_blocks) with unit column
+    stride; seqlens_k int32 (b,) contiguous.  max_seqlen_k defaults to
+    max_blocks * block_size (the host never reads the device-side counts).
+    """
+    if q.dtype not in _DTYPE_CODE or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache, v_cache must share dtype float16 or bfloat16")
+    b, s_q, h, d = q.shape
+    if k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[3] != d:
+        raise ValueError("k_cache and v_cache must be (num_blocks, block_size, h_kv, d)")
+    num_blocks, block_size, h_kv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if h_kv < 1 or h % h_kv != 0:
+        raise ValueError(f"h_kv = {h_kv} must divide h = {h}")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != b \
+            or block_table.stride(1) != 1:
+        raise ValueError("block_table must be int32 (b, max_blocks) with unit column stride")
+    if seqlens_k.dtype != torch.int32 or tuple(seqlens_k.shape) != (b,) or not seqlens_k.is_contiguous():
+        raise ValueError("seqlens_k must be a contiguous int32 (b,) tensor")
+    max_blocks = block_table.shape[1]
+    if max_seqlen_k is None:
+        max_seqlen_k = max_blocks * block_size
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    a = AttnPagedArgs()
+    a.dtype = _DTYPE_CODE[q.dtype]
+    a.causal = 1 if causal else 0
+    a.b, a.s_q, a.h, a.h_kv, a.d = b, s_q, h, h_kv, d
+    a.q, a.q_stride = q.data_ptr(), _bshd("q", q)
+    a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+    a.k_stride, a.v_stride = _bshd("k_cache", k_cache), _bshd("v_cache", v_cache)
+    a.num_blocks, a.block_size = num_blocks, block_size
+    a.block_table, a.block_table_stride, a.max_blocks = block_table.data_ptr(), block_table.stride(0), max_blocks
+    a.seqlens_k, a.max_seqlen_k = seqlens_k.data_ptr(), int(max_seqlen_k)
+    if out is not None:
+        if tuple(out.shape) != (b, s_q, h, d) or out.dtype != q.dtype:
+            raise ValueError("out must match q's shape and dtype")
+        a.o, a.o_stride = out.data_ptr(), _bshd("out", out)
+    if lse is not None:
+        if tuple(lse.shape) != (b, h, s_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 (b, h, s_q) tensor")
+        a.lse = lse.data_ptr()
+    a.softmax_scale = float(softmax_scale)
+    return a
+
+
+def attn_num_splits_paged(b, h, s_q, max_seqlen_k, d, device=None, h_kv=0) -> int:
+    n = ctypes.c_int32(0)
+    dev = torch.cuda.current_device() if device is None else int(device)
+    _check(lib().attn_num_splits_paged(b, h, h_kv, s_q, max_seqlen_k, d, dev, ctypes.byref(n)))
+    return n.value
+
+
+def attn_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, max_seqlen_k=None, softmax_scale=None,
+                   causal=False, out=None, lse=None, stream=None, return_lse=True):
+    """Fused forward over a paged K/V cache. Returns (O, LSE)."""
+    b, s_q, h, d = q.shape
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None and return_lse:
+        lse = torch.empty((b, h, s_q), dtype=torch.float32, device=q.device)
+    a = make_paged_args(q, k_cache, v_cache, block_table, seqlens_k, max_seqlen_k, softmax_scale,
+                        causal, out, lse)
+    _check(lib().attn_fwd_paged(ctypes.byref(a), _stream_ptr(q, stream)))
+    return out, lse
+
+
+def attn_fwd_splitkv_paged(q, k_cache, v_cache, block_table, seqlens_k, num_splits=0, max_seqlen_k=None,
+                           softmax_scale=None, causal=False, o_part=None, lse_part=None, stream=None):
+    """First flash-decoding stage over a paged cache. Returns fp32 (O_parts, LSE_parts)."""
+    a = make_paged_args(q, k_cache, v_cache, block_table, seqlens_k, max_seqlen_k, softmax_scale, causal)
+    b, s_q, h, d = q.shape
+    if num_splits == 0:
+        num_splits = attn_num_splits_paged(b, h, s_q, a.max_seqlen_k, d, q.device.index, h_kv=a.h_kv)
+    if o_part is None:
+        o_part = torch.empty((num_splits, b, h, s_q, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((num_splits, b, h, s_q), dtype=torch.float32, device=q.device)
+    if (tuple(o_part.shape) != (num_splits, b, h, s_q, d) or not o_part.is_contiguous()
+            or tuple(lse_part.shape) != (num_splits, b, h, s_q) or not lse_part.is_contiguous()
+            or o_part.dtype != torch.float32 or lse_part.dtype != torch.float32):
+        raise ValueError("o_part / lse_part must be dense fp32 [n,b,h,s_q,d] / [n,b,h,s_q]")
+    _check(lib().attn_fwd_splitkv_paged(ctypes.byref(a), num_splits, ctypes.c_void_p(o_part.data_ptr()),
+                                        ctypes.c_void_p(lse_part.data_ptr()), _stream_ptr(q, stream)))
+    return o_part, lse_part
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, seqlens_k, num_splits=0, max_seqlen_k=None,
+                      softmax_scale=None, causal=False, stream=None):
+    """Flash-decoding over a paged cache: split-KV stage, then the combine."""
+    o_part, lse_part = attn_fwd_splitkv_paged(q, k_cache, v_cache, block_table, seqlens_k, num_splits,
+                                              max_seqlen_k, softmax_scale, causal, stream=stream)
     return attn_combine(o_part, lse_part, q.dtype, stream=stream)

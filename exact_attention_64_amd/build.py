@@ -17,10 +17,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libattn.so")
 
 # (source, object name, extra flags).  The prefill kernels are compiled once per
-# (input type, causal) pair so that the four sets build in parallel.
+# (input type, causal, paged cache) triple so that the eight sets build in parallel.
 SOURCES = [("attn_api.cpp", "attn_api", []),
-           *[("attn_fwd.hip", f"attn_fwd_t{t}_c{c}", [f"-DATTN_FWD_DTYPE={t}", f"-DATTN_FWD_CAUSAL={c}"])
-             for t in (0, 1) for c in (0, 1)],
+           *[("attn_fwd.hip", f"attn_fwd_t{t}_c{c}_p{g}",
+              [f"-DATTN_FWD_DTYPE={t}", f"-DATTN_FWD_CAUSAL={c}", f"-DATTN_FWD_PAGED={g}"])
+             for t in (0, 1) for c in (0, 1) for g in (0, 1)],
            ("attn_decode.hip", "attn_decode", []),
            ("attn_combine.hip", "attn_combine", [])]
 

@@ -115,6 +115,85 @@ void fill_params(const attn_args* a, attn::FwdParams* p) {
 
 int64_t group_of(const attn_args* a) { return a->h_kv > 0 ? a->h / a->h_kv : 1; }
 
+// Checks of attn_paged_args (same order as check_args).  need_o: O is written.
+attn_status check_paged(const attn_paged_args* a, bool need_o) {
+  if (!a) return ATTN_E_NULL;
+  if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->seqlens_k || (need_o && !a->o))
+    return ATTN_E_NULL;
+  if (a->dtype != ATTN_FP16 && a->dtype != ATTN_BF16) return ATTN_E_DTYPE;
+  attn_status st = check_shape(a->b, a->h, a->s_q, a->max_seqlen_k);
+  if (st != ATTN_OK) return st;
+  if (a->h_kv < 0 || a->h_kv > a->h || (a->h_kv > 0 && a->h % a->h_kv != 0)) return ATTN_E_SHAPE;
+  const int64_t bsz = a->block_size;
+  if (bsz < 32 || bsz > (1 << 20) || (bsz & (bsz - 1)) != 0) return ATTN_E_SHAPE;
+  if (a->num_blocks < 1 || a->num_blocks > 0x7fffffff || a->max_blocks < 1 ||
+      a->block_table_stride < a->max_blocks || a->max_blocks > ATTN_MAX_SEQ ||
+      a->max_seqlen_k > a->max_blocks * bsz)
+    return ATTN_E_SHAPE;
+  if (a->d != 64 && a->d != 128) return ATTN_E_HEADDIM;
+  if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) ||
+      !aligned4(a->block_table) || !aligned4(a->seqlens_k))
+    return ATTN_E_LAYOUT;
+  if (!strides_ok(a->q_stride) || !strides_ok(a->k_stride) || !strides_ok(a->v_stride)) return ATTN_E_LAYOUT;
+  if (need_o && (!aligned16(a->o) || !strides_ok(a->o_stride))) return ATTN_E_LAYOUT;
+  if (need_o && a->lse && !aligned4(a->lse)) return ATTN_E_LAYOUT;
+  if (!std::isfinite(a->softmax_scale)) return ATTN_E_SCALE;
+  return ATTN_OK;
+}
+
+void fill_paged_params(const attn_paged_args* a, attn::FwdParams* p) {
+  std::memset(p, 0, sizeof(*p));
+  p->q = a->q;
+  p->k = a->k_cache;
+  p->v = a->v_cache;
+  p->o = a->o;
+  p->lse = a->lse;
+  for (int i = 0; i < 3; ++i) {
+    p->qs[i] = a->q_stride[i];
+    p->ks[i] = a->k_stride[i];
+    p->vs[i] = a->v_stride[i];
+    p->os[i] = a->o_stride[i];
+  }
+  p->b = (int)a->b;
+  p->h = (int)a->h;
+  p->s_q = (int)a->s_q;
+  p->s_k = (int)a->max_seqlen_k;
+  p->d = (int)a->d;
+  p->n_splits = 1;
+  p->g = a->h_kv > 0 ? (int)(a->h / a->h_kv) : 1;
+  const float s = a->softmax_scale;
+  p->zero_q = s == 0.f;
+  p->neg_q = s < 0.f;
+  p->scale_log2 = s == 0.f ? 1.f : std::fabs(s) * 1.4426950408889634f;
+  p->block_table = a->block_table;
+  p->seqlens_k = a->seqlens_k;
+  p->bt_stride = a->block_table_stride;
+  p->num_blocks = (int)a->num_blocks;
+  int lbs = 0;
+  while ((int64_t(1) << lbs) < a->block_size) ++lbs;
+  p->lbs = lbs;
+}
+
+bool paged_grid_ok(const attn_paged_args* a, int64_t n_splits) {
+  const int64_t g = a->h_kv > 0 ? a->h / a->h_kv : 1;
+  return attn::fwd_groups_per_split(a->b, a->h, g, a->s_q, (int)a->d, true) * n_splits <= 0x7fffffff;
+}
+
+// One split per compute unit's worth of missing work (see attn.h): `work` is the
+// number of work-groups of one split.
+int64_t splits_for_work(int64_t work, int64_t s_k, int64_t num_cus) {
+  int64_t n = 1;
+  if (work < num_cus) {
+    // About one work-group per compute unit (measured best for the one-row
+    // decode kernel: fewer, longer key streams), each split keeping >= 64 keys.
+    n = ceil_div(num_cus, work);
+    n = n < ceil_div(s_k, 64) ? n : ceil_div(s_k, 64);
+    n = n < ATTN_MAX_SPLITS ? n : ATTN_MAX_SPLITS;
+    n = n < 1 ? 1 : n;
+  }
+  return n;
+}
+
 bool grid_ok(const attn_args* a, int64_t n_splits) {
   const int64_t grid = attn::fwd_groups_per_split(a->b, a->h, group_of(a), a->s_q, (int)a->d) * n_splits;
   return grid <= 0x7fffffff;
@@ -165,16 +244,7 @@ attn_status attn_num_splits_kv_for(int64_t b, int64_t h, int64_t h_kv, int64_t s
   // when query heads sharing a K/V head are packed).
   const int64_t g = h_kv > 0 ? h / h_kv : 1;
   const int64_t work = attn::fwd_groups_per_split(b, h, g, s_q, (int)d);
-  int64_t n = 1;
-  if (work < num_cus) {
-    // About one work-group per compute unit (measured best for the one-row
-    // decode kernel: fewer, longer key streams), each split keeping >= 64 keys.
-    n = ceil_div((int64_t)num_cus, work);
-    n = n < ceil_div(s_k, 64) ? n : ceil_div(s_k, 64);
-    n = n < ATTN_MAX_SPLITS ? n : ATTN_MAX_SPLITS;
-    n = n < 1 ? 1 : n;
-  }
-  *n_out = (int32_t)n;
+  *n_out = (int32_t)splits_for_work(work, s_k, num_cus);
   return ATTN_OK;
 }
 
@@ -221,6 +291,57 @@ attn_status attn_fwd_splitkv(const attn_args* a, int32_t num_splits, float* o_pa
   p.n_splits = num_splits;
   hipError_t e = attn::launch_fwd(p, a->dtype, a->causal != 0, true, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+attn_status attn_fwd_paged(const attn_paged_args* a, void* stream) {
+  attn_status st = check_paged(a, true);
+  if (st != ATTN_OK) return st;
+  if (!paged_grid_ok(a, 1)) return ATTN_E_SHAPE;
+  st = current_device_ok();
+  if (st != ATTN_OK) return st;
+  attn::FwdParams p;
+  fill_paged_params(a, &p);
+  hipError_t e = attn::launch_fwd(p, a->dtype, a->causal != 0, false, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+attn_status attn_fwd_splitkv_paged(const attn_paged_args* a, int32_t num_splits, float* o_part,
+                                   float* lse_part, void* stream) {
+  attn_status st = check_paged(a, false);
+  if (st == ATTN_OK && (!o_part || !lse_part)) st = ATTN_E_NULL;
+  if (st != ATTN_OK) return st;
+  if (!aligned16(o_part) || !aligned4(lse_part)) return ATTN_E_LAYOUT;
+  const int64_t max_n = a->max_seqlen_k < ATTN_MAX_SPLITS ? a->max_seqlen_k : ATTN_MAX_SPLITS;
+  if (num_splits < 1 || num_splits > max_n) return ATTN_E_SPLITS;
+  if (!paged_grid_ok(a, num_splits)) return ATTN_E_SHAPE;
+  st = current_device_ok();
+  if (st != ATTN_OK) return st;
+  attn::FwdParams p;
+  fill_paged_params(a, &p);
+  p.o = nullptr;
+  p.lse = nullptr;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.n_splits = num_splits;
+  hipError_t e = attn::launch_fwd(p, a->dtype, a->causal != 0, true, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+attn_status attn_num_splits_paged(int64_t b, int64_t h, int64_t h_kv, int64_t s_q, int64_t max_seqlen_k,
+                                  int64_t d, int device, int32_t* n_out) {
+  if (!n_out) return ATTN_E_NULL;
+  attn_status st = check_shape(b, h, s_q, max_seqlen_k);
+  if (st != ATTN_OK) return st;
+  if (h_kv < 0 || h_kv > h || (h_kv > 0 && h % h_kv != 0)) return ATTN_E_SHAPE;
+  if (d != 64 && d != 128) return ATTN_E_HEADDIM;
+  DevInfo info;
+  st = device_info(device, &info);
+  if (st != ATTN_OK) return st;
+  if (!info.gfx950 || info.cus < 1) return ATTN_E_DEVICE;
+  const int64_t g = h_kv > 0 ? h / h_kv : 1;
+  *n_out = (int32_t)splits_for_work(attn::fwd_groups_per_split(b, h, g, s_q, (int)d, true), max_seqlen_k,
+                                    info.cus);
+  return ATTN_OK;
 }
 
 attn_status attn_combine(int32_t num_splits, int64_t b, int64_t h, int64_t s_q, int64_t d,

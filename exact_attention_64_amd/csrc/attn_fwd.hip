@@ -100,7 +100,13 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, const char* lds) {
 // (batch, K/V head) and its g * s_q query rows, row r being query head
 // hk * g + r / s_q at position r % s_q, so every K/V tile serves the whole group.
 // NT: K/V tiles are read with the nontemporal bit (few work-groups read each tile).
-template <int T_, int D, int BN, int NW, int NBUF, bool PACK, bool NT, bool CAUSAL, bool SPLIT>
+// PAGED: K and V are a block cache, (num_blocks, block_size, h_kv, d) with
+// strides (block, slot, head); key j of batch entry bb is slot j % block_size of
+// block block_table[bb][j / block_size], and the entry has seqlens_k[bb] keys.
+// Block ids and key counts come from device memory, which the host cannot check:
+// they are clamped to [0, num_blocks) and [0, s_k], so no access leaves the
+// cache.  block_size is a power of two >= BN, so a tile touches at most two blocks.
+template <int T_, int D, int BN, int NW, int NBUF, bool PACK, bool NT, bool PAGED, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 64 ? 2 : 4, D >= 64 ? 2 : 4)))
 void fwdp_kernel(const FwdParams p) {
   using Tt = Ty<T_>;
@@ -140,7 +146,9 @@ void fwdp_kernel(const FwdParams p) {
   const int hg = bh - bb * nh;
   const int hk = PACK ? hg : hg / p.g;   // K/V head of the work-group
   const int q0 = qt * BM;
-  const int off = p.s_k - p.s_q;
+  // keys of this batch entry: its own count when paged, else s_k
+  const int s_k = PAGED ? min(max(p.seqlens_k[bb], 0), p.s_k) : p.s_k;
+  const int off = s_k - p.s_q;
   // This lane's row: query head my_h, position my_i (both uniform per
   // work-group unless packed).  Position bounds for the masking decisions are
   // exact for one head's contiguous rows and conservative when packed.
@@ -155,16 +163,17 @@ void fwdp_kernel(const FwdParams p) {
   // fill one wave of eight): such a wave only loads its share of each tile.
   const bool live = !PACK || q0 + wave * 32 < p.g * p.s_q;
 
-  int k_lo = 0, k_hi = p.s_k;
+  int k_lo = 0, k_hi = s_k;
   if (SPLIT) {
-    k_lo = (int)(((int64_t)split * p.s_k) / p.n_splits);
-    k_hi = (int)(((int64_t)(split + 1) * p.s_k) / p.n_splits);
+    k_lo = (int)(((int64_t)split * s_k) / p.n_splits);
+    k_hi = (int)(((int64_t)(split + 1) * s_k) / p.n_splits);
   }
   if (CAUSAL) k_hi = min(k_hi, pos_wg_hi + off + 1);
   const int T = k_hi > k_lo ? (k_hi - k_lo + BN - 1) / BN : 0;
 
-  const unsigned short* __restrict__ Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hk * p.ks[2];
-  const unsigned short* __restrict__ Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hk * p.vs[2];
+  const unsigned short* __restrict__ Kg = (const unsigned short*)p.k + (PAGED ? 0 : (int64_t)bb * p.ks[0]) + (int64_t)hk * p.ks[2];
+  const unsigned short* __restrict__ Vg = (const unsigned short*)p.v + (PAGED ? 0 : (int64_t)bb * p.vs[0]) + (int64_t)hk * p.vs[2];
+  const int* __restrict__ tbl = PAGED ? p.block_table + (int64_t)bb * p.bt_stride : nullptr;
   const int64_t ksr = p.ks[1], vsr = p.vs[1];
 
   // Q fragments (B operand of S^T = K Q^T): this lane's row, d = hi*8 + 16*kk.
@@ -217,6 +226,31 @@ void fwdp_kernel(const FwdParams p) {
                    bool isv, int tile, char* buf, bool full) {
     if (NLW < NW && !loader) return;
     const int k0 = k_lo + tile * BN;
+    if constexpr (PAGED) {
+      // Block of the tile's first key and, when the tile runs past that block
+      // and keys there are in range, the next one (both wave-uniform loads).
+      const int bsz = 1 << p.lbs;
+      const int kb0 = k0 >> p.lbs;
+      const int r0 = k0 - (kb0 << p.lbs);
+      const int blk0 = min(max(tbl[kb0], 0), p.num_blocks - 1);
+      int blk1 = blk0;
+      if (r0 + BN > bsz && ((kb0 + 1) << p.lbs) < k_hi) blk1 = min(max(tbl[kb0 + 1], 0), p.num_blocks - 1);
+      const int64_t bstride = isv ? p.vs[0] : p.ks[0];
+      const bool whole = full || k0 + BN <= k_hi;
+#pragma unroll
+      for (int i = 0; i < WL; ++i) {
+        const int slot = (wave * WL + i) * 64 + lane;
+        const int row = slot / NCH, pc = slot % NCH;
+        const int key = whole ? k0 + row : min(k0 + row, k_hi - 1);  // past the end: re-read the last key
+        const int rel = key - (kb0 << p.lbs);                         // [0, 2 * block_size)
+        const bool second = rel >= bsz;
+        const int64_t blk = second ? blk1 : blk0;
+        const int ch = pc ^ (isv ? Swz<D>::v(row) : Swz<D>::k(row));
+        lds_dma16<NT>((const void*)(G + blk * bstride + (int64_t)(second ? rel - bsz : rel) * gs + ch * 8),
+                      buf + (wave * WL + i) * 1024);
+      }
+      return;
+    }
     if (full || k0 + BN <= k_hi) {
       const unsigned short* __restrict__ Gt = G + (int64_t)k0 * gs;
 #pragma unroll
@@ -490,7 +524,7 @@ void fwdp_kernel(const FwdParams p) {
 // ---------------------------------------------------------------------------
 // Launchers
 
-template <int T_, int D, int BN, int NW, int NBUF, bool PACK, bool CAUSAL, bool SPLIT>
+template <int T_, int D, int BN, int NW, int NBUF, bool PACK, bool PAGED, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwdp_t(const FwdParams& p, hipStream_t st) {
   constexpr int BM = NW * 32;
   FwdParams q = p;
@@ -504,47 +538,51 @@ static hipError_t launch_fwdp_t(const FwdParams& p, hipStream_t st) {
   // them nontemporally measured slower (b = 512, s = 150, h = 16, d = 16).
   if constexpr (D >= 64) {
     if (q.n_qt <= kStreamQTiles) {
-      hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, NW, NBUF, PACK, true, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
+      hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, NW, NBUF, PACK, true, PAGED, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, NW, NBUF, PACK, false, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
+  hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, NW, NBUF, PACK, false, PAGED, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
   return hipGetLastError();
 }
 
-template <int T_, int D, bool CAUSAL, bool SPLIT>
+template <int T_, int D, bool PAGED, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwd_d(const FwdParams& p, hipStream_t st) {
-  // d <= 32: 4 waves (128 query rows) per work-group and up to four waves per SIMD
+  // d <= 32: 4 waves (128 query rows) per work-group and up to four waves per
+  // SIMD; the paged cache is served at d >= 64 only (the host rejects the rest)
   if constexpr (D >= 64) {
     if (fwd_packed(p.g, p.s_q, D))
-      return launch_fwdp_t<T_, D, kPrefillBN, kPrefillNW, kPrefillNBUF, true, CAUSAL, SPLIT>(p, st);
-    return launch_fwdp_t<T_, D, kPrefillBN, kPrefillNW, kPrefillNBUF, false, CAUSAL, SPLIT>(p, st);
+      return launch_fwdp_t<T_, D, kPrefillBN, kPrefillNW, kPrefillNBUF, true, PAGED, CAUSAL, SPLIT>(p, st);
+    return launch_fwdp_t<T_, D, kPrefillBN, kPrefillNW, kPrefillNBUF, false, PAGED, CAUSAL, SPLIT>(p, st);
+  } else if constexpr (!PAGED) {
+    return launch_fwdp_t<T_, D, kPrefillBN, 4, kPrefillNBUF, false, false, CAUSAL, SPLIT>(p, st);
   } else {
-    return launch_fwdp_t<T_, D, kPrefillBN, 4, kPrefillNBUF, false, CAUSAL, SPLIT>(p, st);
+    return hipErrorInvalidValue;
   }
 }
 
-template <int T_, bool CAUSAL, bool SPLIT>
+template <int T_, bool CAUSAL, bool PAGED, bool SPLIT>
 static hipError_t launch_fwd_c(const FwdParams& p, hipStream_t st) {
   switch (p.d) {
-    case 16: return launch_fwd_d<T_, 16, CAUSAL, SPLIT>(p, st);
-    case 32: return launch_fwd_d<T_, 32, CAUSAL, SPLIT>(p, st);
-    case 64: return launch_fwd_d<T_, 64, CAUSAL, SPLIT>(p, st);
-    default: return launch_fwd_d<T_, 128, CAUSAL, SPLIT>(p, st);
+    case 16: return launch_fwd_d<T_, 16, PAGED, CAUSAL, SPLIT>(p, st);
+    case 32: return launch_fwd_d<T_, 32, PAGED, CAUSAL, SPLIT>(p, st);
+    case 64: return launch_fwd_d<T_, 64, PAGED, CAUSAL, SPLIT>(p, st);
+    default: return launch_fwd_d<T_, 128, PAGED, CAUSAL, SPLIT>(p, st);
   }
 }
 
-template <int T_, bool CAUSAL>
+template <int T_, bool CAUSAL, bool PAGED>
 hipError_t launch_prefill_tc(const FwdParams& p, bool split, hipStream_t st) {
-  return split ? launch_fwd_c<T_, CAUSAL, true>(p, st) : launch_fwd_c<T_, CAUSAL, false>(p, st);
+  return split ? launch_fwd_c<T_, CAUSAL, PAGED, true>(p, st) : launch_fwd_c<T_, CAUSAL, PAGED, false>(p, st);
 }
 
-// The library compiles this file once per (input type, causal) pair, selected
-// by ATTN_FWD_DTYPE and ATTN_FWD_CAUSAL, so the four kernel sets build in
-// parallel; launch_prefill (attn_internal.h) picks among them.
-#if !defined(ATTN_FWD_DTYPE) || !defined(ATTN_FWD_CAUSAL)
-#error "compile with -DATTN_FWD_DTYPE=<0|1> -DATTN_FWD_CAUSAL=<0|1>"
+// The library compiles this file once per (input type, causal, paged) triple,
+// selected by ATTN_FWD_DTYPE, ATTN_FWD_CAUSAL and ATTN_FWD_PAGED, so the kernel
+// sets build in parallel; launch_prefill (attn_internal.h) picks among them.
+#if !defined(ATTN_FWD_DTYPE) || !defined(ATTN_FWD_CAUSAL) || !defined(ATTN_FWD_PAGED)
+#error "compile with -DATTN_FWD_DTYPE=<0|1> -DATTN_FWD_CAUSAL=<0|1> -DATTN_FWD_PAGED=<0|1>"
 #endif
-template hipError_t launch_prefill_tc<ATTN_FWD_DTYPE, (ATTN_FWD_CAUSAL != 0)>(const FwdParams&, bool, hipStream_t);
+template hipError_t launch_prefill_tc<ATTN_FWD_DTYPE, (ATTN_FWD_CAUSAL != 0), (ATTN_FWD_PAGED != 0)>(
+    const FwdParams&, bool, hipStream_t);
 
 }  // namespace attn

@@ -29,6 +29,13 @@ struct FwdParams {
   int neg_q;        // softmax_scale < 0: Q is negated on load
   int zero_q;       // softmax_scale == 0: Q is treated as zero
   int g;            // query heads per K/V head: query head hh reads K/V head hh / g
+  // Paged K/V cache (block_table != nullptr): k and v point at the block caches,
+  // ks / vs are the (block, slot, head) strides and s_k bounds every key count.
+  const int* block_table;  // (b, bt_stride) block ids
+  const int* seqlens_k;    // (b) key counts
+  int64_t bt_stride;
+  int num_blocks;
+  int lbs;                 // log2(block_size)
 };
 
 struct CombineParams {
@@ -77,26 +84,37 @@ inline int fwd_rows_per_block(int d, int s_q) {
 // packs a K/V head's g * s_q query rows into its work-groups (d >= 64).
 inline bool fwd_packed(int64_t g, int64_t s_q, int d) { return g > 1 && s_q <= 64 && d >= 64; }
 // Work-groups per split: packed, one per (b, K/V head, block of packed rows);
-// the decode kernel (s_q == 1) puts kDecodeHeads heads in one work-group; the
-// prefill kernel one (b, h, query row block) per work-group.
-inline int64_t fwd_groups_per_split(int64_t b, int64_t h, int64_t g, int64_t s_q, int d) {
+// the decode kernel (s_q == 1, contiguous K/V) puts kDecodeHeads heads in one
+// work-group; the prefill kernel one (b, h, query row block) per work-group.
+// `paged`: the paged cache always runs the prefill kernel.
+inline int64_t fwd_groups_per_split(int64_t b, int64_t h, int64_t g, int64_t s_q, int d, bool paged = false) {
   const int64_t bm = d >= 64 ? kPrefillNW * 32 : 4 * 32;  // prefill rows per work-group
   if (fwd_packed(g, s_q, d)) return b * (h / g) * ((g * s_q + bm - 1) / bm);
-  if (s_q == 1) return (b * h + kDecodeHeads - 1) / kDecodeHeads;
+  if (s_q == 1 && !paged) return (b * h + kDecodeHeads - 1) / kDecodeHeads;
   return b * h * ((s_q + bm - 1) / bm);
 }
 
 // Fused / split-KV prefill kernel (s_q >= 1; used for s_q > 1), one explicit
 // instantiation per (input type, causal) pair in its own object file.
-template <int T_, bool CAUSAL>
+template <int T_, bool CAUSAL, bool PAGED>
 hipError_t launch_prefill_tc(const FwdParams& p, bool split, hipStream_t st);
-extern template hipError_t launch_prefill_tc<kFP16, false>(const FwdParams&, bool, hipStream_t);
-extern template hipError_t launch_prefill_tc<kFP16, true>(const FwdParams&, bool, hipStream_t);
-extern template hipError_t launch_prefill_tc<kBF16, false>(const FwdParams&, bool, hipStream_t);
-extern template hipError_t launch_prefill_tc<kBF16, true>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_prefill_tc<kFP16, false, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_prefill_tc<kFP16, true, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_prefill_tc<kBF16, false, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_prefill_tc<kBF16, true, false>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_prefill_tc<kFP16, false, true>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_prefill_tc<kFP16, true, true>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_prefill_tc<kBF16, false, true>(const FwdParams&, bool, hipStream_t);
+extern template hipError_t launch_prefill_tc<kBF16, true, true>(const FwdParams&, bool, hipStream_t);
+template <bool PAGED>
+inline hipError_t launch_prefill_p(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st) {
+  if (dtype == kBF16)
+    return causal ? launch_prefill_tc<kBF16, true, PAGED>(p, split, st) : launch_prefill_tc<kBF16, false, PAGED>(p, split, st);
+  return causal ? launch_prefill_tc<kFP16, true, PAGED>(p, split, st) : launch_prefill_tc<kFP16, false, PAGED>(p, split, st);
+}
 inline hipError_t launch_prefill(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st) {
-  if (dtype == kBF16) return causal ? launch_prefill_tc<kBF16, true>(p, split, st) : launch_prefill_tc<kBF16, false>(p, split, st);
-  return causal ? launch_prefill_tc<kFP16, true>(p, split, st) : launch_prefill_tc<kFP16, false>(p, split, st);
+  return p.block_table ? launch_prefill_p<true>(p, dtype, causal, split, st)
+                       : launch_prefill_p<false>(p, dtype, causal, split, st);
 }
 // One-row decode kernel (s_q == 1).
 hipError_t launch_decode(const FwdParams& p, int dtype, bool split, hipStream_t st);
@@ -105,8 +123,8 @@ hipError_t launch_decode(const FwdParams& p, int dtype, bool split, hipStream_t 
 // group).  With one query row the bottom-right causal mask hides nothing, so the
 // causal flag does not matter there.
 inline hipError_t launch_fwd(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st) {
-  return p.s_q == 1 && !fwd_packed(p.g, p.s_q, p.d) ? launch_decode(p, dtype, split, st)
-                                                     : launch_prefill(p, dtype, causal, split, st);
+  return p.s_q == 1 && !fwd_packed(p.g, p.s_q, p.d) && !p.block_table ? launch_decode(p, dtype, split, st)
+                                                                       : launch_prefill(p, dtype, causal, split, st);
 }
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t st);
 

@@ -155,6 +155,64 @@ attn_status attn_combine(int32_t num_splits, int64_t b, int64_t h, int64_t s_q, 
                          const float *o_part, const float *lse_part, int32_t dtype,
                          void *o, const int64_t o_stride[3], float *lse, void *stream);
 
+/* Paged K/V cache.  "LLM Lab Notes 07" (section 5, "Engineering Takeaways")
+ * names the paged KV cache as the standard companion of the fused kernel for
+ * long contexts and gives no layout; this library takes the plainest one:
+ *   - k_cache, v_cache: blocks of block_size keys, (num_blocks, block_size, h_kv,
+ *     d) with element strides k_stride / v_stride for (block, slot, head), each
+ *     a non-negative multiple of 8, d contiguous, base pointers 16-byte aligned;
+ *   - block_table: device int32, b rows of max_blocks entries, rows
+ *     block_table_stride (>= max_blocks) elements apart: key j of sequence bi is
+ *     slot j % block_size of block block_table[bi][j / block_size];
+ *   - seqlens_k: device int32 (b): the key count of each sequence (0 allowed);
+ *     max_seqlen_k (host, >= 1) bounds every count and must not exceed
+ *     max_blocks * block_size.
+ * Each sequence attends over its own keys: with causal != 0 query i of sequence
+ * bi sees key j iff j <= i + seqlens_k[bi] - s_q, and in attn_fwd_splitkv_paged
+ * split i covers keys [floor(i*s/n), floor((i+1)*s/n)) of its own count s.  Q, O
+ * and LSE are laid out as in attn_args.  block_size is a power of two in [32,
+ * 2^20] and d is 64 or 128 (else ATTN_E_SHAPE / ATTN_E_HEADDIM).  The table and
+ * the counts live in device memory and cannot be checked on the host: the kernel
+ * clamps block ids to [0, num_blocks) and counts to [0, max_seqlen_k], so
+ * malformed entries give wrong results, never an access outside the cache.
+ * Every shape and pointer rule of attn_args applies otherwise. */
+typedef struct {
+  int32_t dtype;        /* attn_dtype of Q, the caches and O */
+  int32_t causal;
+  int64_t b, s_q, h, h_kv, d;   /* h_kv: 0 means h; else h must be a multiple of it */
+  const void *q;        /* device pointer, (b, s_q, h, d) */
+  int64_t q_stride[3];  /* element strides of Q for (b, s, h) */
+  const void *k_cache;  /* device pointer, (num_blocks, block_size, h_kv, d) */
+  const void *v_cache;
+  int64_t k_stride[3];  /* element strides for (block, slot, head) */
+  int64_t v_stride[3];
+  int64_t num_blocks, block_size;
+  const int32_t *block_table;   /* device pointer, (b, max_blocks), 4-byte aligned */
+  int64_t block_table_stride, max_blocks;
+  const int32_t *seqlens_k;     /* device pointer, (b), 4-byte aligned */
+  int64_t max_seqlen_k;
+  void *o;              /* device pointer, (b, s_q, h, d), written by attn_fwd_paged */
+  int64_t o_stride[3];
+  float *lse;           /* dense (b, h, s_q) fp32, may be NULL; attn_fwd_paged only */
+  float softmax_scale;
+} attn_paged_args;
+
+/* Fused forward over a paged cache: O and LSE in one kernel (as attn_fwd). */
+attn_status attn_fwd_paged(const attn_paged_args *args, void *stream);
+
+/* First flash-decoding stage over a paged cache: partials laid out as written by
+ * attn_fwd_splitkv (combine them with attn_combine); num_splits in [1,
+ * min(max_seqlen_k, ATTN_MAX_SPLITS)].  args->o, o_stride and lse are ignored. */
+attn_status attn_fwd_splitkv_paged(const attn_paged_args *args, int32_t num_splits,
+                                   float *o_part, float *lse_part, void *stream);
+
+/* Split count for attn_fwd_splitkv_paged: the rule of attn_num_splits_kv with
+ * s_k = max_seqlen_k, counting the prefill kernel's work-groups (one per (b, h,
+ * query row block), or per (b, K/V head, packed row block) when packed), which
+ * the paged cache uses for every s_q. */
+attn_status attn_num_splits_paged(int64_t b, int64_t h, int64_t h_kv, int64_t s_q,
+                                  int64_t max_seqlen_k, int64_t d, int device, int32_t *n_out);
+
 /* Static, human-readable text for a status code. */
 const char *attn_status_str(int32_t status);
 

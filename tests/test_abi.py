@@ -60,6 +60,85 @@ int main(void) {
     assert got == want
 
 
+def test_paged_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "paged.c"
+    fields = ["b", "h_kv", "q", "q_stride", "k_cache", "v_cache", "k_stride", "v_stride", "num_blocks",
+              "block_size", "block_table", "block_table_stride", "max_blocks", "seqlens_k", "max_seqlen_k",
+              "o", "o_stride", "lse", "softmax_scale"]
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"attn.h\"\nint main(void) {\n"
+                   '  printf("%zu\\n", sizeof(attn_paged_args));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(attn_paged_args, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "paged"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    A = _lib.AttnPagedArgs
+    assert got == [ctypes.sizeof(A)] + [getattr(A, f).offset for f in fields]
+
+
+def _paged(**kw):
+    a = _lib.AttnPagedArgs()
+    a.dtype, a.causal = _lib.ATTN_BF16, 0
+    a.b, a.s_q, a.h, a.h_kv, a.d = 2, 4, 8, 2, 128
+    a.q = a.k_cache = a.v_cache = a.o = a.lse = FAKE
+    a.block_table = a.seqlens_k = FAKE
+    a.q_stride = _lib.I64x3(4 * 8 * 128, 8 * 128, 128)
+    a.k_stride = a.v_stride = _lib.I64x3(64 * 2 * 128, 2 * 128, 128)
+    a.num_blocks, a.block_size = 10, 64
+    a.block_table_stride, a.max_blocks = 4, 4
+    a.max_seqlen_k = 256
+    a.o_stride = a.q_stride
+    a.softmax_scale = 0.125
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+PAGED_BAD = [
+    ("null_table", dict(block_table=None), -1),
+    ("null_seqlens", dict(seqlens_k=None), -1),
+    ("null_cache", dict(v_cache=None), -1),
+    ("dtype", dict(dtype=3), -2),
+    ("max_seqlen_0", dict(max_seqlen_k=0), -3),
+    ("max_seqlen_beyond_table", dict(max_seqlen_k=257), -3),
+    ("block_size_not_pow2", dict(block_size=48), -3),
+    ("block_size_16", dict(block_size=16, max_seqlen_k=64), -3),
+    ("table_stride_short", dict(block_table_stride=3), -3),
+    ("no_blocks", dict(num_blocks=0), -3),
+    ("h_kv_not_divisor", dict(h_kv=3), -3),
+    ("headdim_32", dict(d=32), -4),
+    ("misaligned_table", dict(block_table=FAKE + 2), -5),
+    ("misaligned_cache", dict(k_cache=FAKE + 8), -5),
+    ("cache_stride_not_mult8", dict(k_stride=_lib.I64x3(64 * 2 * 128, 2 * 128 + 4, 128)), -5),
+    ("scale_nan", dict(softmax_scale=float("nan")), -6),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", PAGED_BAD, ids=[b[0] for b in PAGED_BAD])
+def test_paged_validation(name, kw, code):
+    a = _paged(**kw)
+    assert ea.lib().attn_fwd_paged(ctypes.byref(a), None) == code
+    assert ea.lib().attn_fwd_splitkv_paged(ctypes.byref(a), 2, FAKE, FAKE, None) == code
+
+
+def test_paged_split_count_and_partials_checked():
+    L = ea.lib()
+    a = _paged()
+    assert L.attn_fwd_splitkv_paged(ctypes.byref(a), 0, FAKE, FAKE, None) == -7
+    assert L.attn_fwd_splitkv_paged(ctypes.byref(a), 257, FAKE, FAKE, None) == -7
+    assert L.attn_fwd_splitkv_paged(ctypes.byref(a), 2, None, FAKE, None) == -1
+    assert L.attn_fwd_splitkv_paged(ctypes.byref(a), 2, FAKE + 4, FAKE, None) == -5
+    a2 = _paged(max_seqlen_k=5)   # at most 5 splits
+    assert L.attn_fwd_splitkv_paged(ctypes.byref(a2), 6, FAKE, FAKE, None) == -7
+    assert L.attn_fwd_paged(None, None) == -1
+    n = ctypes.c_int32()
+    assert L.attn_num_splits_paged(1, 8, 2, 1, 100, 32, 0, ctypes.byref(n)) == -4
+    assert L.attn_num_splits_paged(1, 8, 3, 1, 100, 128, 0, ctypes.byref(n)) == -3
+    assert L.attn_num_splits_paged(1, 8, 2, 1, 100, 128, 0, None) == -1
+
+
 def _args(**kw):
     a = _lib.AttnArgs()
     a.dtype, a.causal = _lib.ATTN_BF16, 0

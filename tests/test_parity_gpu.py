@@ -286,6 +286,89 @@ def test_multi_token_decode_48_heads(s_q):
     check(O2, L2, O_ref, L_ref, "bf16", f"s_q={s_q} split (heuristic)")
 
 
+PAGED_CASES = [
+    # dtype, b, s_q, h, h_kv, d, seqlens, block_size, causal, splits
+    ("bf16", 3, 1, 16, 2, 128, [1000, 0, 77], 64, False, 4),     # packed decode, an empty sequence
+    ("fp16", 2, 1, 4, 4, 128, [513, 2048], 32, False, 8),       # one row per head, block = tile
+    ("bf16", 2, 7, 12, 3, 64, [300, 7], 128, True, 3),          # packed multi-token, s_k == s_q
+    ("fp16", 2, 300, 4, 2, 128, [333, 290], 256, True, 1),      # chunked prefill; rows with no key
+    ("bf16", 1, 3, 8, 1, 128, [4096], 1024, False, 5),
+    ("fp16", 3, 2, 6, 6, 64, [95, 1, 64], 32, True, 2),
+]
+
+
+def _paged_case(case):
+    dt, b, s_q, h, h_kv, d, lens, bs, causal, n = case
+    q, kc, vc, table, sl = workloads.make_paged(b, s_q, h, d, dt, lens, bs, h_kv=h_kv, seed=29)
+    return q, kc, vc, table, sl
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=[f"{c[0]}-b{c[1]}-q{c[2]}-h{c[3]}-kv{c[4]}-d{c[5]}-bs{c[7]}-n{c[9]}" for c in PAGED_CASES])
+def test_paged_kv_cache(case):
+    dt, b, s_q, h, h_kv, d, lens, bs, causal, n = case
+    say("paged K/V cache", case)
+    q, kc, vc, table, sl = _paged_case(case)
+    scale = 1 / math.sqrt(d)
+    O_ref, L_ref = oracle.attention_paged(*host64(q, kc, vc), table.numpy(), sl.numpy(), scale, causal)
+    qd, kcd, vcd, td, sld = upload(q, kc, vc, table, sl)
+    O, L = ea.attn_fwd_paged(qd, kcd, vcd, td, sld, softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    check(O, L, O_ref, L_ref, dt, f"{case} fused")
+    Op, Lp = ea.attn_fwd_splitkv_paged(qd, kcd, vcd, td, sld, num_splits=n, softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    Op_ref, Lp_ref = oracle.attention_split_paged(*host64(q, kc, vc), table.numpy(), sl.numpy(), scale,
+                                                  causal, n)
+    Lp_h = f64(Lp)
+    fin = np.isfinite(Lp_ref)
+    assert np.array_equal(np.isfinite(Lp_h), fin)
+    if fin.any():
+        assert np.abs(Lp_h[fin] - Lp_ref[fin]).max() <= TOL_LSE
+    assert np.abs(f64(Op) - Op_ref).max() <= TOL_O[dt]
+    O2, L2 = ea.attn_combine(Op, Lp, q.dtype)
+    torch.cuda.synchronize()
+    check(O2, L2, O_ref, L_ref, dt, f"{case} split")
+
+
+def test_paged_unused_table_entries_are_not_read():
+    # entries past each sequence's last block hold ids far outside the cache; the
+    # kernel never reads them (an exact bound, not the clamp, keeps them out)
+    say("paged cache, junk table tail")
+    case = ("bf16", 3, 4, 8, 2, 128, [100, 64, 1], 64, True, 3)
+    q, kc, vc, table, sl = _paged_case(case)
+    for bi, n in enumerate(case[6]):
+        used = -(-n // 64)
+        table[bi, used:] = torch.tensor([10 ** 9, -5, 7 * 10 ** 8])[: table.shape[1] - used]
+    scale = 0.125
+    ok = table.clone()
+    ok[ok < 0] = 0
+    ok[ok >= kc.shape[0]] = 0
+    O_ref, L_ref = oracle.attention_paged(*host64(q, kc, vc), ok.numpy(), sl.numpy(), scale, True)
+    qd, kcd, vcd, td, sld = upload(q, kc, vc, table, sl)
+    for n in (1, 2, 3):
+        O, L = ea.attn_decode_paged(qd, kcd, vcd, td, sld, num_splits=n, softmax_scale=scale, causal=True)
+        torch.cuda.synchronize()
+        check(O, L, O_ref, L_ref, "bf16", f"junk tail n={n}")
+
+
+def test_paged_matches_contiguous_layout():
+    # a cache whose blocks hold each sequence in order (identity table) against the
+    # contiguous entry points on the same tensors, packed decode and prefill
+    say("paged vs contiguous")
+    for (b, s_q, s_k, h, h_kv) in ((2, 1, 2048, 16, 2), (1, 130, 512, 4, 4)):
+        q, k, v = workloads.make_qkv(b, s_q, s_k, h, 128, "bf16", seed=31, h_kv=h_kv)
+        bs = 64
+        kc = k.reshape(b * s_k // bs, bs, h_kv, 128)
+        vc = v.reshape(b * s_k // bs, bs, h_kv, 128)
+        table = torch.arange(b * s_k // bs, dtype=torch.int32).reshape(b, s_k // bs)
+        sl = torch.full((b,), s_k, dtype=torch.int32)
+        qd, kd, vd, kcd, vcd, td, sld = upload(q, k, v, kc, vc, table, sl)
+        O1, L1 = ea.attn_fwd(qd, kd, vd, causal=True)
+        O2, L2 = ea.attn_fwd_paged(qd, kcd, vcd, td, sld, causal=True)
+        torch.cuda.synchronize()
+        assert (O1.float() - O2.float()).abs().max().item() <= TOL_O["bf16"]
+        assert (L1 - L2).abs().max().item() <= TOL_LSE
+
+
 def test_combine_identical_splits_adds_ln2():
     say("attn_combine identical splits")
     g = torch.Generator().manual_seed(3)
