@@ -100,6 +100,16 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, const char* lds) {
 // (batch, K/V head) and its g * s_q query rows, row r being query head
 // hk * g + r / s_q at position r % s_q, so every K/V tile serves the whole group.
 // NT: K/V tiles are read with the nontemporal bit (few work-groups read each tile).
+// One wave-uniform 32-bit read through the scalar data cache (read only).  The
+// compiler would issue a block-table read as a vector load (the DMA helper's
+// memory clobber keeps it from proving the table unchanged), and waiting for
+// that load would mean waiting for every K/V load in flight before it.
+__device__ __forceinline__ int sload_i32(const int* ptr) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr));
+  return v;
+}
+
 // PAGED: K and V are a block cache, (num_blocks, block_size, h_kv, d) with
 // strides (block, slot, head); key j of batch entry bb is slot j % block_size of
 // block block_table[bb][j / block_size], and the entry has seqlens_k[bb] keys.
@@ -232,9 +242,9 @@ void fwdp_kernel(const FwdParams p) {
       const int bsz = 1 << p.lbs;
       const int kb0 = k0 >> p.lbs;
       const int r0 = k0 - (kb0 << p.lbs);
-      const int blk0 = min(max(tbl[kb0], 0), p.num_blocks - 1);
+      const int blk0 = min(max(sload_i32(tbl + kb0), 0), p.num_blocks - 1);
       int blk1 = blk0;
-      if (r0 + BN > bsz && ((kb0 + 1) << p.lbs) < k_hi) blk1 = min(max(tbl[kb0 + 1], 0), p.num_blocks - 1);
+      if (r0 + BN > bsz && ((kb0 + 1) << p.lbs) < k_hi) blk1 = min(max(sload_i32(tbl + kb0 + 1), 0), p.num_blocks - 1);
       const int64_t bstride = isv ? p.vs[0] : p.ks[0];
       const bool whole = full || k0 + BN <= k_hi;
 #pragma unroll
