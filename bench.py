@@ -305,6 +305,45 @@ def main():
                               io_gbs=round(io / (med * 1e-3) / 1e9, 1),
                               frac_mfma=round(flops(w) / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
             del q, k, v, O, L
+        # Multi-token decode with shared K/V heads (b=8, 48 query heads over 8 K/V
+        # heads, a 4096-key cache, 1 or 4 new tokens): split-KV + combine with the
+        # heuristic's split count, over the contiguous cache and over a paged one
+        # (64-key blocks, scattered), one event pair around both launches after a
+        # cache flush, mean of 20 passes.
+        for s_q in (1, 4):
+            q, k, v = (t.to(dev) for t in workloads.make_qkv(8, s_q, 4096, 48, 128, "bf16", seed=19, h_kv=8))
+            _, kc, vc, table, sl = (t.to(dev) for t in workloads.make_paged(8, s_q, 48, 128, "bf16", [4096] * 8,
+                                                                             64, h_kv=8, seed=19))
+            kvb = 2 * k.numel() * 2
+            for kind in ("contiguous", "paged"):
+                if kind == "contiguous":
+                    n = ea.attn_num_splits(8, 48, s_q, 4096, 128, h_kv=8)
+                    run = lambda: ea.attn_fwd_splitkv(q, k, v, n, None, True, o_part=op, lse_part=lp)  # noqa: E731
+                else:
+                    n = ea.attn_num_splits_paged(8, 48, s_q, 4096, 128, h_kv=8)
+                    run = lambda: ea.attn_fwd_splitkv_paged(q, kc, vc, table, sl, n, 4096, None, True,  # noqa: E731
+                                                            o_part=op, lse_part=lp)
+                op = torch.empty((n, 8, 48, s_q, 128), dtype=torch.float32, device=dev)
+                lp = torch.empty((n, 8, 48, s_q), dtype=torch.float32, device=dev)
+                O = torch.empty_like(q)
+                run()
+                ts = []
+                for _ in range(20):
+                    flush_s.fill_(0.0)
+                    a, b = E(), E()
+                    a.record()
+                    run()
+                    ea.attn_combine(op, lp, q.dtype, out=O, lse=None, return_lse=False)
+                    b.record()
+                    torch.cuda.synchronize()
+                    ts.append(a.elapsed_time(b))
+                mean = sum(ts) / len(ts)
+                side[f"gqa_decode_{kind}_s_q{s_q}"] = dict(
+                    workload=f"bf16 causal b=8 s_q={s_q} s_k=4096 h=48 h_kv=8 d=128, {kind} K/V"
+                             + (" (64-key blocks)" if kind == "paged" else "") + ", split-KV + combine",
+                    us=round(mean * 1e3, 2), splits=n, kv_gbs=round(kvb / (mean * 1e-3) / 1e9, 1),
+                    frac_hbm=round(kvb / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+            del q, k, v, kc, vc, table, sl, op, lp, O
         del flush_s
 
     out = {
