@@ -305,6 +305,32 @@ def main():
                               io_gbs=round(io / (med * 1e-3) / 1e9, 1),
                               frac_mfma=round(flops(w) / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
             del q, k, v, O, L
+        # The tiny workload through a HIP graph: 16 calls captured once, the graph
+        # replayed 50 times between one event pair; device time and host time per call.
+        w = W["C1"]
+        q, k, v = (t.to(dev) for t in workloads.make_workload(w))
+        O = torch.empty_like(q)
+        L = torch.empty((w.b, w.h, w.s_q), dtype=torch.float32, device=dev)
+        ea.attn_fwd(q, k, v, w.scale, w.causal, out=O, lse=L)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(16):
+                ea.attn_fwd(q, k, v, w.scale, w.causal, out=O, lse=L)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = E(), E()
+        h0 = time.perf_counter()
+        a.record()
+        for _ in range(50):
+            g.replay()
+        b.record()
+        host_us = (time.perf_counter() - h0) / (50 * 16) * 1e6
+        torch.cuda.synchronize()
+        dev_us = a.elapsed_time(b) / (50 * 16) * 1e3
+        side["C1_graph"] = dict(workload=w.note + ", 16 calls per HIP graph replay", us_per_call=round(dev_us, 2),
+                                host_us_per_call=round(host_us, 2), calls=50 * 16)
+        del g, q, k, v, O, L
         # Multi-token decode with shared K/V heads (b=8, 48 query heads over 8 K/V
         # heads, a 4096-key cache, 1 or 4 new tokens): split-KV + combine with the
         # heuristic's split count, over the contiguous cache and over a paged one
