@@ -176,7 +176,7 @@ void fill_paged_params(const attn_paged_args* a, attn::FwdParams* p) {
 
 bool paged_grid_ok(const attn_paged_args* a, int64_t n_splits) {
   const int64_t g = a->h_kv > 0 ? a->h / a->h_kv : 1;
-  return attn::fwd_groups_per_split(a->b, a->h, g, a->s_q, (int)a->d, true) * n_splits <= 0x7fffffff;
+  return attn::fwd_groups_per_split(a->b, a->h, g, a->s_q, (int)a->d) * n_splits <= 0x7fffffff;
 }
 
 // One split per compute unit's worth of missing work (see attn.h): `work` is the
@@ -339,8 +339,7 @@ attn_status attn_num_splits_paged(int64_t b, int64_t h, int64_t h_kv, int64_t s_
   if (st != ATTN_OK) return st;
   if (!info.gfx950 || info.cus < 1) return ATTN_E_DEVICE;
   const int64_t g = h_kv > 0 ? h / h_kv : 1;
-  *n_out = (int32_t)splits_for_work(attn::fwd_groups_per_split(b, h, g, s_q, (int)d, true), max_seqlen_k,
-                                    info.cus);
+  *n_out = (int32_t)splits_for_work(attn::fwd_groups_per_split(b, h, g, s_q, (int)d), max_seqlen_k, info.cus);
   return ATTN_OK;
 }
 

@@ -30,16 +30,32 @@ __device__ __forceinline__ float slot_sum(float x) {
   return x;
 }
 
-template <int T_, int D, bool SPLIT>
+// Three wave-uniform 32-bit reads through the scalar data cache (read only),
+// waited for together.
+__device__ __forceinline__ void sload3_i32(const int* a, const int* b, const int* c, int& x, int& y, int& z) {
+  asm volatile("s_load_dword %0, %3, 0x0\n\ts_load_dword %1, %4, 0x0\n\ts_load_dword %2, %5, 0x0\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&s"(x), "=&s"(y), "=&s"(z)
+               : "s"(a), "s"(b), "s"(c));
+}
+
+// PAGED: K and V are a block cache (num_blocks, block_size, h_kv, d) with
+// (block, slot, head) strides; key j of batch entry bb is slot j % block_size of
+// block block_table[bb][j / block_size], and the entry has seqlens_k[bb] keys.
+// One batch of U * KPI <= 64 keys touches at most three blocks (block_size >= 32);
+// their ids are read once per batch with scalar loads and each lane picks its
+// key's block.  Ids are clamped to [0, num_blocks), key counts to [0, s_k].
+template <int T_, int D, bool SPLIT, bool PAGED>
 __global__ __launch_bounds__(kDecodeHeads * 64) void decode_kernel(const FwdParams p) {
   using Tt = Ty<T_>;
   using Dt = Dot<T_>;
   constexpr int LPH = D / 8;        // lanes per key row
   constexpr int KPI = 64 / LPH;     // keys per wave load (= slots per wave)
   constexpr int U = kDecodeBatch;   // wave loads per tensor in one batch
+  static_assert(!PAGED || U * KPI <= 64, "a paged batch must span at most three 32-key blocks");
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slot = lane / LPH;
   const int dc = lane % LPH;
   // 1-D grid, split fastest: work-group g covers split g % n_splits of head
@@ -50,10 +66,11 @@ __global__ __launch_bounds__(kDecodeHeads * 64) void decode_kernel(const FwdPara
   const int bb = bh / p.h;
   const int hh = bh - bb * p.h;
 
-  int k_lo = 0, k_hi = p.s_k;
+  const int s_k = PAGED ? min(max(p.seqlens_k[bb], 0), p.s_k) : p.s_k;
+  int k_lo = 0, k_hi = s_k;
   if (SPLIT) {
-    k_lo = (int)(((int64_t)split * p.s_k) / p.n_splits);
-    k_hi = (int)(((int64_t)(split + 1) * p.s_k) / p.n_splits);
+    k_lo = (int)(((int64_t)split * s_k) / p.n_splits);
+    k_hi = (int)(((int64_t)(split + 1) * s_k) / p.n_splits);
   }
   const int ws = k_lo, we = k_hi;
 
@@ -63,9 +80,13 @@ __global__ __launch_bounds__(kDecodeHeads * 64) void decode_kernel(const FwdPara
     if (p.neg_q) q ^= 0x80008000u;
   }
   const int hk = hh / p.g;  // K/V head of this query head
-  const unsigned short* __restrict__ Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hk * p.ks[2] + dc * 8;
-  const unsigned short* __restrict__ Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hk * p.vs[2] + dc * 8;
+  const unsigned short* __restrict__ Kg =
+      (const unsigned short*)p.k + (PAGED ? 0 : (int64_t)bb * p.ks[0]) + (int64_t)hk * p.ks[2] + dc * 8;
+  const unsigned short* __restrict__ Vg =
+      (const unsigned short*)p.v + (PAGED ? 0 : (int64_t)bb * p.vs[0]) + (int64_t)hk * p.vs[2] + dc * 8;
   const int64_t ksr = p.ks[1], vsr = p.vs[1];
+  const int* __restrict__ tbl = PAGED ? p.block_table + (int64_t)bb * p.bt_stride : nullptr;
+  const int last_blk = PAGED && we > 0 ? (we - 1) >> p.lbs : 0;  // last block with a key of this split
   const float c = p.scale_log2;
 
   float m = -INFINITY, l = 0.f;
@@ -78,13 +99,30 @@ __global__ __launch_bounds__(kDecodeHeads * 64) void decode_kernel(const FwdPara
   // compile-time constants and the buffers stay in registers).
   u32x4_t kb0[U], vb0[U], kb1[U], vb1[U];
   auto load = [&](u32x4_t (&kb)[U], u32x4_t (&vb)[U], int j0) {
+    int blk[3] = {0, 0, 0};
+    int kb0 = 0;
+    if constexpr (PAGED) {
+      kb0 = j0 >> p.lbs;
+      sload3_i32(tbl + kb0, tbl + min(kb0 + 1, last_blk), tbl + min(kb0 + 2, last_blk), blk[0], blk[1], blk[2]);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) blk[i] = min(max(blk[i], 0), p.num_blocks - 1);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u * KPI + slot;
       u32x4_t xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
       if (j < we) {
-        xk = __builtin_nontemporal_load((const u32x4_t*)(Kg + (int64_t)j * ksr));
-        xv = __builtin_nontemporal_load((const u32x4_t*)(Vg + (int64_t)j * vsr));
+        int64_t ko = (int64_t)j * ksr, vo = (int64_t)j * vsr;
+        if constexpr (PAGED) {
+          const int rel = j - (kb0 << p.lbs);          // [0, 3 * block_size)
+          const int bi = rel >> p.lbs;
+          const int64_t b = bi == 0 ? blk[0] : (bi == 1 ? blk[1] : blk[2]);
+          const int r = rel & ((1 << p.lbs) - 1);
+          ko = b * p.ks[0] + (int64_t)r * ksr;
+          vo = b * p.vs[0] + (int64_t)r * vsr;
+        }
+        xk = __builtin_nontemporal_load((const u32x4_t*)(Kg + ko));
+        xv = __builtin_nontemporal_load((const u32x4_t*)(Vg + vo));
       }
       kb[u] = xk;
       vb[u] = xv;
@@ -167,11 +205,17 @@ static hipError_t launch_decode_t(const FwdParams& p, hipStream_t st) {
   const int64_t groups = ((int64_t)p.b * p.h + kDecodeHeads - 1) / kDecodeHeads;
   const dim3 grid((unsigned)(groups * p.n_splits));
   const dim3 block(kDecodeHeads * 64);
+  if (p.block_table) {  // paged cache: d is 64 or 128 (checked on the host)
+    if (p.d == 64) hipLaunchKernelGGL((decode_kernel<T_, 64, SPLIT, true>), grid, block, 0, st, p);
+    else if (p.d == 128) hipLaunchKernelGGL((decode_kernel<T_, 128, SPLIT, true>), grid, block, 0, st, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   switch (p.d) {
-    case 16: hipLaunchKernelGGL((decode_kernel<T_, 16, SPLIT>), grid, block, 0, st, p); break;
-    case 32: hipLaunchKernelGGL((decode_kernel<T_, 32, SPLIT>), grid, block, 0, st, p); break;
-    case 64: hipLaunchKernelGGL((decode_kernel<T_, 64, SPLIT>), grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<T_, 128, SPLIT>), grid, block, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((decode_kernel<T_, 16, SPLIT, false>), grid, block, 0, st, p); break;
+    case 32: hipLaunchKernelGGL((decode_kernel<T_, 32, SPLIT, false>), grid, block, 0, st, p); break;
+    case 64: hipLaunchKernelGGL((decode_kernel<T_, 64, SPLIT, false>), grid, block, 0, st, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<T_, 128, SPLIT, false>), grid, block, 0, st, p); break;
   }
   return hipGetLastError();
 }

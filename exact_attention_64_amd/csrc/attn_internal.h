@@ -84,13 +84,12 @@ inline int fwd_rows_per_block(int d, int s_q) {
 // packs a K/V head's g * s_q query rows into its work-groups (d >= 64).
 inline bool fwd_packed(int64_t g, int64_t s_q, int d) { return g > 1 && s_q <= 64 && d >= 64; }
 // Work-groups per split: packed, one per (b, K/V head, block of packed rows);
-// the decode kernel (s_q == 1, contiguous K/V) puts kDecodeHeads heads in one
-// work-group; the prefill kernel one (b, h, query row block) per work-group.
-// `paged`: the paged cache always runs the prefill kernel.
-inline int64_t fwd_groups_per_split(int64_t b, int64_t h, int64_t g, int64_t s_q, int d, bool paged = false) {
+// the decode kernel (s_q == 1) puts kDecodeHeads heads in one work-group; the
+// prefill kernel one (b, h, query row block) per work-group.
+inline int64_t fwd_groups_per_split(int64_t b, int64_t h, int64_t g, int64_t s_q, int d) {
   const int64_t bm = d >= 64 ? kPrefillNW * 32 : 4 * 32;  // prefill rows per work-group
   if (fwd_packed(g, s_q, d)) return b * (h / g) * ((g * s_q + bm - 1) / bm);
-  if (s_q == 1 && !paged) return (b * h + kDecodeHeads - 1) / kDecodeHeads;
+  if (s_q == 1) return (b * h + kDecodeHeads - 1) / kDecodeHeads;
   return b * h * ((s_q + bm - 1) / bm);
 }
 
@@ -123,8 +122,8 @@ hipError_t launch_decode(const FwdParams& p, int dtype, bool split, hipStream_t 
 // group).  With one query row the bottom-right causal mask hides nothing, so the
 // causal flag does not matter there.
 inline hipError_t launch_fwd(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st) {
-  return p.s_q == 1 && !fwd_packed(p.g, p.s_q, p.d) && !p.block_table ? launch_decode(p, dtype, split, st)
-                                                                       : launch_prefill(p, dtype, causal, split, st);
+  return p.s_q == 1 && !fwd_packed(p.g, p.s_q, p.d) ? launch_decode(p, dtype, split, st)
+                                                     : launch_prefill(p, dtype, causal, split, st);
 }
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t st);
 

@@ -294,6 +294,8 @@ PAGED_CASES = [
     ("fp16", 2, 300, 4, 2, 128, [333, 290], 256, True, 1),      # chunked prefill; rows with no key
     ("bf16", 1, 3, 8, 1, 128, [4096], 1024, False, 5),
     ("fp16", 3, 2, 6, 6, 64, [95, 1, 64], 32, True, 2),
+    ("bf16", 3, 1, 5, 5, 64, [1000, 0, 33], 32, True, 7),       # one-row decode kernel: 64-key batches
+    ("bf16", 2, 1, 3, 3, 128, [4097, 31], 64, False, 3),        # over three 32-key blocks; mixed lengths
 ]
 
 
@@ -329,11 +331,12 @@ def test_paged_kv_cache(case):
     check(O2, L2, O_ref, L_ref, dt, f"{case} split")
 
 
-def test_paged_unused_table_entries_are_not_read():
+@pytest.mark.parametrize("s_q,h_kv", [(4, 2), (1, 8)])
+def test_paged_unused_table_entries_are_not_read(s_q, h_kv):
     # entries past each sequence's last block hold ids far outside the cache; the
-    # kernel never reads them (an exact bound, not the clamp, keeps them out)
-    say("paged cache, junk table tail")
-    case = ("bf16", 3, 4, 8, 2, 128, [100, 64, 1], 64, True, 3)
+    # kernels never read them (an exact bound, not the clamp, keeps them out)
+    say("paged cache, junk table tail", s_q, h_kv)
+    case = ("bf16", 3, s_q, 8, h_kv, 128, [100, 64, 1], 64, True, 3)
     q, kc, vc, table, sl = _paged_case(case)
     for bi, n in enumerate(case[6]):
         used = -(-n // 64)
