@@ -69,6 +69,15 @@ template <int D> struct Swz {
 // lose terms that are negligible against the row's maximum.
 template <int N> struct IC { static constexpr int value = N; };
 
+// f(IC<I>{}), ..., f(IC<N - 1>{}), unrolled at compile time.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IC<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // One direct-to-LDS wave load: lane i copies 16 bytes from gptr to LDS byte
 // address lds + 16 i (lds is wave-uniform).  Written as inline asm so that the
 // compiler does not treat the LDS write as aliasing the reads of other ring
@@ -131,7 +140,7 @@ void fwdp_kernel(const FwdParams p) {
   constexpr int NLW = NLOAD < NW ? NLOAD : NW;  // waves that take part in the loads
   constexpr int WL = NLOAD / NLW;               // loads per taking-part wave
   static_assert(NLOAD >= 1 && NLOAD % NLW == 0, "a tile must split into 1 KB wave loads");
-  static_assert(NBUF == 2 || NBUF == 4, "the step loop is unrolled by NBUF");
+  static_assert(NBUF == 2 || NBUF == 4 || NBUF == 8, "the step loop is unrolled by NBUF");
   constexpr int P = NBUF - 1;                   // prefetch distance in tiles
   constexpr int PAIR = 2 * WL;                  // loads of one (K, V) pair per wave
   constexpr float PMAX = 0x1p64f;               // bound on a partial row sum of P
@@ -462,28 +471,17 @@ void fwdp_kernel(const FwdParams p) {
   if (CAUSAL) t_clean = min(t_clean, (pos_wg_lo + off - k_lo + 1) / BN);
   if (T > 0) iter(IC<0>{}, 0, true, sA, sB, pB, pA, kbuf[0], kbuf[1], vbuf[NBUF - 2], vbuf[NBUF - 1]);
   int t = 1;
-  for (; t + NBUF <= t_clean; t += NBUF) {
-    step(IC<2>{}, t, IC<1 % NBUF>{});
-    step(IC<2>{}, t + 1, IC<2 % NBUF>{});
-    if constexpr (NBUF == 4) {
-      step(IC<2>{}, t + 2, IC<3>{});
-      step(IC<2>{}, t + 3, IC<0>{});
-    }
-  }
-  for (; t + NBUF < T; t += NBUF) {
-    step(IC<1>{}, t, IC<1 % NBUF>{});
-    step(IC<1>{}, t + 1, IC<2 % NBUF>{});
-    if constexpr (NBUF == 4) {
-      step(IC<1>{}, t + 2, IC<3>{});
-      step(IC<1>{}, t + 3, IC<0>{});
-    }
-  }
-  if (t < T) step(IC<0>{}, t, IC<1 % NBUF>{});
-  if (t + 1 < T) step(IC<0>{}, t + 1, IC<2 % NBUF>{});
-  if constexpr (NBUF == 4) {
-    if (t + 2 < T) step(IC<0>{}, t + 2, IC<3>{});
-    if (t + 3 < T) step(IC<0>{}, t + 3, IC<0>{});
-  }
+  for (; t + NBUF <= t_clean; t += NBUF)
+    static_for<0, NBUF>([&](auto I) __attribute__((always_inline)) {
+      step(IC<2>{}, t + I.value, IC<(I.value + 1) % NBUF>{});
+    });
+  for (; t + NBUF < T; t += NBUF)
+    static_for<0, NBUF>([&](auto I) __attribute__((always_inline)) {
+      step(IC<1>{}, t + I.value, IC<(I.value + 1) % NBUF>{});
+    });
+  static_for<0, NBUF>([&](auto I) __attribute__((always_inline)) {
+    if (t + I.value < T) step(IC<0>{}, t + I.value, IC<(I.value + 1) % NBUF>{});
+  });
   if (T >= 1 && live) {
     u32x4_t vf[CB][NT16];
     read_v(vbuf[(T - 1) % NBUF], vf);
@@ -534,7 +532,7 @@ void fwdp_kernel(const FwdParams p) {
 // ---------------------------------------------------------------------------
 // Launchers
 
-template <int T_, int D, int BN, int NW, int NBUF, bool PACK, bool PAGED, bool CAUSAL, bool SPLIT>
+template <int T_, int D, int NW, bool PACK, bool NT, bool PAGED, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwdp_t(const FwdParams& p, hipStream_t st) {
   constexpr int BM = NW * 32;
   FwdParams q = p;
@@ -542,18 +540,27 @@ static hipError_t launch_fwdp_t(const FwdParams& p, hipStream_t st) {
   const int64_t nh = PACK ? p.h / p.g : p.h;
   q.n_qt = (int)((rows + BM - 1) / BM);
   const int64_t grid = (int64_t)q.n_qt * p.b * nh * p.n_splits;
-  // Nontemporal K/V loads when at most kStreamQTiles work-groups read each tile
-  // and a key row fills whole 128-byte lines (d >= 64): shorter rows share
-  // lines with the neighbouring heads that other work-groups read, and reading
-  // them nontemporally measured slower (b = 512, s = 150, h = 16, d = 16).
-  if constexpr (D >= 64) {
-    if (q.n_qt <= kStreamQTiles) {
-      hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, NW, NBUF, PACK, true, PAGED, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((fwdp_kernel<T_, D, BN, NW, NBUF, PACK, false, PAGED, CAUSAL, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
+  hipLaunchKernelGGL((fwdp_kernel<T_, D, kPrefillBN, NW, kPrefillNBUF, PACK, NT, PAGED, CAUSAL, SPLIT>),
+                     dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
   return hipGetLastError();
+}
+
+// Launch shape at d >= 64 from the rows one head (or packed group) brings:
+//  - at most 128 (decode and short chunks): 4 waves, so two work-groups share a
+//    compute unit and twice as many key streams are in flight (measured 1.66x
+//    faster than 8 waves on b = 8, h = 48, s_q = 4, 4096 keys);
+//  - otherwise 8 waves (256 rows) sharing each K/V tile.
+// K/V loads are nontemporal when at most kStreamQTiles work-groups read each
+// tile.  (At d <= 32 a key row is 32 or 64 bytes and shares its cache lines with
+// the neighbouring heads that other work-groups read; reading those
+// nontemporally measured slower, b = 512, s = 150, h = 16, d = 16.)
+template <int T_, int D, bool PACK, bool PAGED, bool CAUSAL, bool SPLIT>
+static hipError_t launch_fwd_rows(const FwdParams& p, hipStream_t st) {
+  const int64_t rows = PACK ? (int64_t)p.g * p.s_q : p.s_q;
+  if (rows <= 4 * 32) return launch_fwdp_t<T_, D, 4, PACK, true, PAGED, CAUSAL, SPLIT>(p, st);
+  if ((rows + kPrefillNW * 32 - 1) / (kPrefillNW * 32) <= kStreamQTiles)
+    return launch_fwdp_t<T_, D, kPrefillNW, PACK, true, PAGED, CAUSAL, SPLIT>(p, st);
+  return launch_fwdp_t<T_, D, kPrefillNW, PACK, false, PAGED, CAUSAL, SPLIT>(p, st);
 }
 
 template <int T_, int D, bool PAGED, bool CAUSAL, bool SPLIT>
@@ -561,11 +568,10 @@ static hipError_t launch_fwd_d(const FwdParams& p, hipStream_t st) {
   // d <= 32: 4 waves (128 query rows) per work-group and up to four waves per
   // SIMD; the paged cache is served at d >= 64 only (the host rejects the rest)
   if constexpr (D >= 64) {
-    if (fwd_packed(p.g, p.s_q, D))
-      return launch_fwdp_t<T_, D, kPrefillBN, kPrefillNW, kPrefillNBUF, true, PAGED, CAUSAL, SPLIT>(p, st);
-    return launch_fwdp_t<T_, D, kPrefillBN, kPrefillNW, kPrefillNBUF, false, PAGED, CAUSAL, SPLIT>(p, st);
+    return fwd_packed(p.g, p.s_q, D) ? launch_fwd_rows<T_, D, true, PAGED, CAUSAL, SPLIT>(p, st)
+                                     : launch_fwd_rows<T_, D, false, PAGED, CAUSAL, SPLIT>(p, st);
   } else if constexpr (!PAGED) {
-    return launch_fwdp_t<T_, D, kPrefillBN, 4, kPrefillNBUF, false, false, CAUSAL, SPLIT>(p, st);
+    return launch_fwdp_t<T_, D, 4, false, false, false, CAUSAL, SPLIT>(p, st);
   } else {
     return hipErrorInvalidValue;
   }

@@ -51,12 +51,14 @@ struct CombineParams {
 // Compile-time tunables (overridable with -D for sweeps).
 #ifndef ATTN_PREFILL_NW
 #define ATTN_PREFILL_NW 8   // waves per work-group of the d >= 64 prefill kernel (32 rows each)
+                            // when a head (or packed group) has more than 128 query rows
 #endif
 #ifndef ATTN_PREFILL_BN
 #define ATTN_PREFILL_BN 32  // keys per tile of the d >= 64 prefill kernel
 #endif
 #ifndef ATTN_PREFILL_NBUF
-#define ATTN_PREFILL_NBUF 4 // LDS ring buffers per tensor (prefetch depth + 1), 2 or 4
+#define ATTN_PREFILL_NBUF 4 // LDS ring buffers per tensor (prefetch depth + 1): 2, 4 or 8
+                            // (packed decode: 2 measured 25% slower, 8 10% slower)
 #endif
 #ifndef ATTN_STREAM_QTILES
 #define ATTN_STREAM_QTILES 2 // prefill K/V loads are nontemporal when at most this many work-groups read a tile
@@ -74,12 +76,6 @@ constexpr int kStreamQTiles = ATTN_STREAM_QTILES;
 constexpr int kDecodeHeads = ATTN_DECODE_HEADS;
 constexpr int kDecodeBatch = ATTN_DECODE_BATCH;
 
-// Query rows covered by one work-group for head dim d and s_q query rows: the
-// decode kernel (s_q == 1) takes one row; the prefill kernel NW x 32 rows
-// (d >= 64) or 4 x 32 rows (d <= 32).
-inline int fwd_rows_per_block(int d, int s_q) {
-  return s_q == 1 ? 1 : (d >= 64 ? kPrefillNW * 32 : 4 * 32);
-}
 // Query heads sharing a K/V head (g > 1) with few query rows: the prefill kernel
 // packs a K/V head's g * s_q query rows into its work-groups (d >= 64).
 inline bool fwd_packed(int64_t g, int64_t s_q, int d) { return g > 1 && s_q <= 64 && d >= 64; }

@@ -71,6 +71,8 @@ SMALL = [
     ("fp16", 1, 33, 65, 3, 16),
     ("bf16", 1, 1, 700, 4, 128),   # one query row (decode shape) through the fused kernel
     ("fp16", 1, 700, 5, 2, 128),   # fewer keys than rows: causal rows at the top see nothing
+    ("bf16", 2, 128, 300, 3, 128), # at most 128 rows per head: the 4-wave launch
+    ("fp16", 1, 100, 90, 2, 64),   # the same with rows that see no key
 ]
 
 
