@@ -32,7 +32,7 @@ I64x3 = ctypes.c_int64 * 3
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_num_splits", "attn_num_splits_for", "attn_num_splits_kv",
            "attn_num_splits_kv_for", "attn_fwd_splitkv", "attn_combine", "attn_fwd_paged",
-           "attn_fwd_splitkv_paged", "attn_num_splits_paged", "attn_status_str")
+           "attn_fwd_splitkv_paged", "attn_num_splits_paged", "attn_bwd", "attn_status_str")
 
 
 class AttnArgs(ctypes.Structure):
@@ -64,6 +64,24 @@ class AttnPagedArgs(ctypes.Structure):
         ("max_blocks", ctypes.c_int64),
         ("seqlens_k", ctypes.c_void_p), ("max_seqlen_k", ctypes.c_int64),
         ("o", ctypes.c_void_p), ("o_stride", I64x3), ("lse", ctypes.c_void_p),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class AttnBwdArgs(ctypes.Structure):
+    """Mirror of ``attn_bwd_args`` in include/attn.h."""
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("b", ctypes.c_int64), ("s_q", ctypes.c_int64), ("s_k", ctypes.c_int64),
+        ("h", ctypes.c_int64), ("h_kv", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("dout", ctypes.c_void_p),
+        ("q_stride", I64x3), ("k_stride", I64x3), ("v_stride", I64x3), ("o_stride", I64x3),
+        ("dout_stride", I64x3),
+        ("lse", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("dq_stride", I64x3), ("dk_stride", I64x3), ("dv_stride", I64x3),
+        ("delta", ctypes.c_void_p),
         ("softmax_scale", ctypes.c_float),
     ]
 
@@ -116,6 +134,8 @@ def lib():
             L.attn_fwd_splitkv_paged.restype = ctypes.c_int32
             L.attn_num_splits_paged.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, P(ctypes.c_int32)]
             L.attn_num_splits_paged.restype = ctypes.c_int32
+            L.attn_bwd.argtypes = [P(AttnBwdArgs), ctypes.c_void_p]
+            L.attn_bwd.restype = ctypes.c_int32
             L.attn_status_str.argtypes = [ctypes.c_int32]
             L.attn_status_str.restype = ctypes.c_char_p
             _lib = L
@@ -349,3 +369,62 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seqlens_k, num_splits=0,
     o_part, lse_part = attn_fwd_splitkv_paged(q, k_cache, v_cache, block_table, seqlens_k, num_splits,
                                               max_seqlen_k, softmax_scale, causal, stream=stream)
     return attn_combine(o_part, lse_part, q.dtype, stream=stream)
+
+
+# ---------------------------------------------------------------- backward ----
+
+def make_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, delta, softmax_scale=None,
+                  causal=False) -> AttnBwdArgs:
+    """Fill ``attn_bwd_args`` (no copies)."""
+    if q.dtype not in _DTYPE_CODE or any(t.dtype != q.dtype for t in (k, v, out, dout, dq, dk, dv)):
+        raise TypeError("q, k, v, out, dout, dq, dk, dv must share dtype float16 or bfloat16")
+    b, s_q, h, d = q.shape
+    if k.dim() != 4:
+        raise ValueError("k and v must be 4-D (b, s_k, h_kv, d)")
+    s_k, h_kv = k.shape[1], k.shape[2]
+    kshape = (b, s_k, h_kv, d)
+    if tuple(v.shape) != kshape or h_kv < 1 or h % h_kv != 0:
+        raise ValueError(f"k and v must be (b, s_k, h_kv, d) = ({b}, s_k, h_kv, {d}) with h_kv dividing {h}")
+    for name, t, shp in (("out", out, q.shape), ("dout", dout, q.shape), ("dq", dq, q.shape),
+                         ("dk", dk, kshape), ("dv", dv, kshape)):
+        if tuple(t.shape) != tuple(shp):
+            raise ValueError(f"{name} must have shape {tuple(shp)}, got {tuple(t.shape)}")
+    for name, t in (("lse", lse), ("delta", delta)):
+        if tuple(t.shape) != (b, h, s_q) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 (b, h, s_q) tensor")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    a = AttnBwdArgs()
+    a.dtype = _DTYPE_CODE[q.dtype]
+    a.causal = 1 if causal else 0
+    a.b, a.s_q, a.s_k, a.h, a.h_kv, a.d = b, s_q, s_k, h, h_kv, d
+    a.q, a.k, a.v, a.o, a.dout = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr()
+    a.q_stride, a.k_stride, a.v_stride = _bshd("q", q), _bshd("k", k), _bshd("v", v)
+    a.o_stride, a.dout_stride = _bshd("out", out), _bshd("dout", dout)
+    a.lse = lse.data_ptr()
+    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    a.dq_stride, a.dk_stride, a.dv_stride = _bshd("dq", dq), _bshd("dk", dk), _bshd("dv", dv)
+    a.delta = delta.data_ptr()
+    a.softmax_scale = float(softmax_scale)
+    return a
+
+
+def attn_bwd(q, k, v, out, dout, lse, softmax_scale=None, causal=False, dq=None, dk=None, dv=None,
+             delta=None, stream=None):
+    """Gradient of exact attention: returns (dq, dk, dv) in q's dtype.
+
+    ``out`` and ``lse`` are the forward's outputs for the same q, k, v, scale and
+    causal flag; ``delta`` is the (b, h, s_q) fp32 workspace (allocated when None).
+    """
+    b, s_q, h, d = q.shape
+    if dq is None:
+        dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if dk is None:
+        dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    if dv is None:
+        dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    if delta is None:
+        delta = torch.empty((b, h, s_q), dtype=torch.float32, device=q.device)
+    a = make_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, delta, softmax_scale, causal)
+    _check(lib().attn_bwd(ctypes.byref(a), _stream_ptr(q, stream)))
+    return dq, dk, dv

@@ -23,16 +23,22 @@ SOURCES = [("attn_api.cpp", "attn_api", []),
               [f"-DATTN_FWD_DTYPE={t}", f"-DATTN_FWD_CAUSAL={c}", f"-DATTN_FWD_PAGED={g}"])
              for t in (0, 1) for c in (0, 1) for g in (0, 1)],
            ("attn_decode.hip", "attn_decode", []),
-           ("attn_combine.hip", "attn_combine", [])]
+           ("attn_combine.hip", "attn_combine", []),
+           ("attn_bwd.hip", "attn_bwd", [])]
+
+# Translation units whose MFMA accumulators may live in AGPRs: the dK/dV kernel
+# keeps two fp32 accumulator sets (dK^T, dV^T) next to its K and V operands,
+# more than the 256 VGPRs of a lane.
+AGPR_SOURCES = {"attn_bwd.hip"}
 
 # Packed fp32 VALU instructions are switched off for every HIP translation unit.
-# MFMA accumulators are kept in VGPRs (the prefill kernel's vector ALU works on
-# the score tile the matrix core produces; AGPR-held scores would cost a copy
-# per element).
+# Outside AGPR_SOURCES, MFMA accumulators are kept in VGPRs (the forward
+# kernels' vector ALU works on the score tile the matrix core produces;
+# AGPR-held scores would cost a copy per element).
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wno-unused-command-line-argument"]
+VGPR_ACC_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:
@@ -50,7 +56,8 @@ def build(verbose: bool = False) -> str:
     for src, name, extra in SOURCES:
         obj = os.path.join(HERE, "_build", name + ".o")
         os.makedirs(os.path.dirname(obj), exist_ok=True)
-        cmd = [cc, *HIP_FLAGS, *extra, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
+        acc = [] if src in AGPR_SOURCES else VGPR_ACC_FLAGS
+        cmd = [cc, *HIP_FLAGS, *acc, *extra, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd.insert(1, "-x")
             cmd.insert(2, "hip")

@@ -343,6 +343,68 @@ attn_status attn_num_splits_paged(int64_t b, int64_t h, int64_t h_kv, int64_t s_
   return ATTN_OK;
 }
 
+attn_status attn_bwd(const attn_bwd_args* a, void* stream) {
+  if (!a) return ATTN_E_NULL;
+  if (!a->q || !a->k || !a->v || !a->o || !a->dout || !a->lse || !a->dq || !a->dk || !a->dv || !a->delta)
+    return ATTN_E_NULL;
+  if (a->dtype != ATTN_FP16 && a->dtype != ATTN_BF16) return ATTN_E_DTYPE;
+  attn_status st = check_shape(a->b, a->h, a->s_q, a->s_k);
+  if (st != ATTN_OK) return st;
+  if (a->h_kv < 0 || a->h_kv > a->h || (a->h_kv > 0 && a->h % a->h_kv != 0)) return ATTN_E_SHAPE;
+  const int64_t g = a->h_kv > 0 ? a->h / a->h_kv : 1;
+  if (!headdim_ok(a->d)) return ATTN_E_HEADDIM;
+  // grids: delta (d/8 lanes per (b, row, head), 256 per work-group), dQ (128
+  // query rows), dK/dV (128 keys); every one must fit a 32-bit grid dimension
+  if (ceil_div(a->b * a->s_q * a->h * (a->d / 8), 256) > 0x7fffffff ||
+      a->b * a->h * ceil_div(a->s_q, 128) > 0x7fffffff || a->b * (a->h / g) * ceil_div(a->s_k, 128) > 0x7fffffff)
+    return ATTN_E_SHAPE;
+  const void* t16[] = {a->q, a->k, a->v, a->o, a->dout, a->dq, a->dk, a->dv};
+  for (const void* t : t16)
+    if (!aligned16(t)) return ATTN_E_LAYOUT;
+  if (!aligned4(a->lse) || !aligned4(a->delta)) return ATTN_E_LAYOUT;
+  const int64_t* strides[] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride,
+                              a->dout_stride, a->dq_stride, a->dk_stride, a->dv_stride};
+  for (const int64_t* s : strides)
+    if (!strides_ok(s)) return ATTN_E_LAYOUT;
+  if (!std::isfinite(a->softmax_scale)) return ATTN_E_SCALE;
+  st = current_device_ok();
+  if (st != ATTN_OK) return st;
+  attn::BwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.o = a->o;
+  p.dout = a->dout;
+  p.lse = a->lse;
+  p.delta = a->delta;
+  p.dq = a->dq;
+  p.dk = a->dk;
+  p.dv = a->dv;
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = a->q_stride[i];
+    p.ks[i] = a->k_stride[i];
+    p.vs[i] = a->v_stride[i];
+    p.os[i] = a->o_stride[i];
+    p.dos[i] = a->dout_stride[i];
+    p.dqs[i] = a->dq_stride[i];
+    p.dks[i] = a->dk_stride[i];
+    p.dvs[i] = a->dv_stride[i];
+  }
+  p.b = (int)a->b;
+  p.h = (int)a->h;
+  p.s_q = (int)a->s_q;
+  p.s_k = (int)a->s_k;
+  p.d = (int)a->d;
+  p.g = (int)g;
+  // base 2 inside the kernels: P = exp2(scale*log2(e) * q.k - LSE*log2(e));
+  // the sign of the scale stays in it (the forward's LSE already carries it)
+  p.scale = a->softmax_scale;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  hipError_t e = attn::launch_bwd(p, a->dtype, a->causal != 0, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
 attn_status attn_combine(int32_t num_splits, int64_t b, int64_t h, int64_t s_q, int64_t d,
                          const float* o_part, const float* lse_part, int32_t dtype, void* o,
                          const int64_t o_stride[3], float* lse, void* stream) {

@@ -1,0 +1,451 @@
+// Backward of exact attention for gfx950 (MI355X): dQ, dK, dV for an upstream
+// gradient dO, from the forward's O and per-row LSE.
+//
+// flash-attention issue #1335 ("2.6.3 is faster than 2.7.0 for flash-attn v2
+// CUDA fwd/bwd") times this backward on its fp16, head-dim-16 workloads without
+// describing the algorithm; what it computes is the gradient of the standard
+// attention of "LLM Lab Notes 07: Why FlashAttention Is Fast" (section 2), here
+// evaluated tile by tile like the forward, so that neither P nor dS reaches
+// device memory (sections 3.1, 3.2).  Per (batch, head), with c = scale*log2(e)
+// and the forward's natural-log LSE:
+//   P_ij  = exp2(c*q_i.k_j - LSE_i*log2(e))      (the forward's softmax, exactly)
+//   dV_j  = sum_i P_ij dO_i
+//   dP_ij = dO_i . v_j,   delta_i = dO_i . O_i
+//   dS_ij = P_ij (dP_ij - delta_i)
+//   dQ_i  = scale * sum_j dS_ij k_j,   dK_j = scale * sum_i dS_ij q_i
+// Three kernels, all deterministic (no atomics):
+//   bwd_delta_kernel : delta (b, h, s_q) fp32 = row dot of dO and O;
+//   bwd_dq_kernel    : one work-group per (b, query head, 128 query rows); K and V
+//                      tiles of 32 keys stream through LDS; S^T, dP^T and dS^T are
+//                      formed so that each lane owns one query row (the forward's
+//                      layout) and dQ^T += K^T dS^T accumulates in registers;
+//   bwd_dkdv_kernel  : one work-group per (b, K/V head, 128 keys); Q and dO tiles
+//                      of 32 rows (of every query head of the group) stream
+//                      through LDS; S, dP and dS are formed so that each lane owns
+//                      one key, and dV^T += dO^T P, dK^T += Q^T dS accumulate in
+//                      registers.  Query heads sharing a K/V head are summed in
+//                      the same work-group, in a fixed order.
+// Every product runs on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulation;
+// P and dS are rounded to the input type before they feed a product.
+#include "attn_common.h"
+
+namespace attn {
+namespace {
+
+// A 32-row tile of D elements in LDS, rows padded by 16 bytes so that a column
+// of 16-byte chunks read by 16 lanes falls on distinct banks.
+template <int D> struct BTile {
+  static constexpr int RS = D * 2 + 16;  // bytes per row
+  static constexpr int BYTES = 32 * RS;
+  static constexpr int NCH = D / 8;      // 16-byte chunks per row
+  static constexpr int CHUNKS = 32 * NCH;
+  static constexpr int NPT = (CHUNKS + 255) / 256;  // chunks per thread (256 threads)
+};
+
+// global -> registers -> LDS staging of one 32-row tile by the 256 threads of a
+// work-group.  Rows at or past `nrows` re-read row nrows - 1 (finite data; the
+// kernels mask or discard what those rows produce).
+template <int D> struct Stage {
+  u32x4_t r[BTile<D>::NPT];
+  __device__ __forceinline__ void load(const unsigned short* __restrict__ G, int64_t rs, int row0, int nrows,
+                                       int tid) {
+#pragma unroll
+    for (int i = 0; i < BTile<D>::NPT; ++i) {
+      const int c = tid + 256 * i;
+      if (c < BTile<D>::CHUNKS) {
+        const int row = min(row0 + c / BTile<D>::NCH, nrows - 1);
+        r[i] = *(const u32x4_t*)(G + (int64_t)row * rs + (c % BTile<D>::NCH) * 8);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < BTile<D>::NPT; ++i) {
+      const int c = tid + 256 * i;
+      if (c < BTile<D>::CHUNKS)
+        *(u32x4_t*)(lds + (c / BTile<D>::NCH) * BTile<D>::RS + (c % BTile<D>::NCH) * 16) = r[i];
+    }
+  }
+};
+
+// Row-major fragment of a 32-row LDS tile: lane (l32, hi) gets elements
+// [8*hi + 16*kk, +8) of row l32, the A (or B) operand layout of the 32x32x16
+// product along D.
+template <int D>
+__device__ __forceinline__ u32x4_t frag_rows(const char* t, int l32, int hi, int kk) {
+  return *(const u32x4_t*)(t + l32 * BTile<D>::RS + 16 * (hi + 2 * kk));
+}
+
+// Transposed fragment of a 32-row LDS tile: the A operand of a product whose
+// M index is the tile's column (cb*32 + l32) and whose K index runs over the
+// tile's rows.  For K chunk t16 the lane holds rows 16*t16 + 4*hi + {0..3} and
+// 16*t16 + 8 + 4*hi + {0..3}, the rows that lane owns in an accumulator block
+// of the 32x32 product (element r at row (r/4)*8 + 4*hi + r%4), so an
+// accumulator converted in place is the matching B operand.  Each half comes
+// from one ds_read_b64_tr_b16, in which lane x of a 16-lane group fetches 4
+// columns of row x/4 and receives column x of the 4 rows.  At D = 16 the upper
+// 16 columns repeat the lower ones.
+template <int D>
+__device__ __forceinline__ u32x4_t frag_cols(const char* t, int lane, int hi, int cb, int t16) {
+  const int g16 = (lane >> 4) & 1, xr = (lane & 15) >> 2, xq = lane & 3;
+  const int col = (cb * 32 + g16 * 16 + xq * 4) & (D >= 32 ? 0x7fffffff : D - 1);
+  u32x4_t f;
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int row = 16 * t16 + 8 * rd + 4 * hi + xr;
+    const char* a = t + row * BTile<D>::RS + col * 2;
+    const u32x2_t y = bitcast<u32x2_t>(__builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(a)));
+    f[2 * rd] = y[0];
+    f[2 * rd + 1] = y[1];
+  }
+  return f;
+}
+
+// Store a lane's accumulated column: element r of block cb is d = cb*32 +
+// (r/4)*8 + 4*hi + r%4, times `mul`, rounded to the storage type.
+template <int T_, int D, int CB>
+__device__ __forceinline__ void store_cols(unsigned short* __restrict__ dst, const f32x16_t (&acc)[CB], int hi,
+                                           float mul) {
+  using Tt = Ty<T_>;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int col = cb * 32 + r4 * 8 + hi * 4;
+      if (col >= D) continue;
+      u32x2_t x = {Tt::pack2(acc[cb][4 * r4] * mul, acc[cb][4 * r4 + 1] * mul),
+                   Tt::pack2(acc[cb][4 * r4 + 2] * mul, acc[cb][4 * r4 + 3] * mul)};
+      *(u32x2_t*)(dst + col) = x;
+    }
+}
+
+// log2-domain LSE of a row: +inf for a row that sees no key (LSE = -inf), so
+// that exp2(s*c - lse2) = 0 there.
+__device__ __forceinline__ float lse_log2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// delta_i = dO_i . O_i in fp32; D/8 lanes per (row, head), 16 bytes each.
+template <int T_, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p) {
+  constexpr int NL = D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t pair = gid / NL;
+  const int part = (int)(gid % NL);
+  const int64_t total = (int64_t)p.b * p.s_q * p.h;
+  const bool ok = pair < total;
+  float acc = 0.f;
+  int hh = 0, i = 0, bb = 0;
+  if (ok) {
+    hh = (int)(pair % p.h);
+    const int64_t rest = pair / p.h;
+    i = (int)(rest % p.s_q);
+    bb = (int)(rest / p.s_q);
+    const u32x4_t a = *(const u32x4_t*)((const unsigned short*)p.dout + (int64_t)bb * p.dos[0] +
+                                         (int64_t)i * p.dos[1] + (int64_t)hh * p.dos[2] + part * 8);
+    const u32x4_t o = *(const u32x4_t*)((const unsigned short*)p.o + (int64_t)bb * p.os[0] +
+                                         (int64_t)i * p.os[1] + (int64_t)hh * p.os[2] + part * 8);
+    float fa[8], fo[8];
+    Dot<T_>::unpack8(a, fa);
+    Dot<T_>::unpack8(o, fo);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(fa[e], fo[e], acc);
+  }
+  // The NL lanes of a (row, head) are consecutive and NL divides 64, so a
+  // group never spans waves and is either wholly in range or wholly out.
+#pragma unroll
+  for (int m = NL / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 64);
+  if (ok && part == 0) p.delta[((int64_t)bb * p.h + hh) * p.s_q + i] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one work-group = 4 waves x 32 query rows of one (b, query head).
+template <int T_, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
+  using Tt = Ty<T_>;
+  constexpr int KK = D / 16, CB = D >= 32 ? D / 32 : 1, BM = 128;
+  __shared__ __attribute__((aligned(16))) char kbuf[2][BTile<D>::BYTES];
+  __shared__ __attribute__((aligned(16))) char vbuf[2][BTile<D>::BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_qt = (p.s_q + BM - 1) / BM;
+  const int per = p.b * p.h;
+  const int qt_rev = blockIdx.x / per;
+  const int bh = blockIdx.x - qt_rev * per;
+  const int qt = CAUSAL ? n_qt - 1 - qt_rev : qt_rev;  // causal: heaviest tiles first
+  const int bb = bh / p.h, hh = bh - bb * p.h, hk = hh / p.g;
+  const int q0 = qt * BM;
+  const int my_i = q0 + wave * 32 + l32;
+  const bool row_ok = my_i < p.s_q;
+  const int off = p.s_k - p.s_q;
+  int k_hi = p.s_k;
+  if (CAUSAL) k_hi = min(k_hi, q0 + BM - 1 + off + 1);
+  const int T = k_hi > 0 ? (k_hi + 31) / 32 : 0;
+
+  // Q and dO of this lane's row: B operands of S^T = K Q^T and dP^T = V dO^T.
+  u32x4_t qf[KK], df[KK];
+  float lse2 = INFINITY, dl = 0.f;
+  {
+    const unsigned short* Qr = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)my_i * p.qs[1] +
+                               (int64_t)hh * p.qs[2];
+    const unsigned short* Dr = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] +
+                               (int64_t)my_i * p.dos[1] + (int64_t)hh * p.dos[2];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4_t z = {0u, 0u, 0u, 0u};
+      qf[kk] = row_ok ? *(const u32x4_t*)(Qr + hi * 8 + kk * 16) : z;
+      df[kk] = row_ok ? *(const u32x4_t*)(Dr + hi * 8 + kk * 16) : z;
+    }
+    if (row_ok) {
+      const int64_t ri = ((int64_t)bb * p.h + hh) * p.s_q + my_i;
+      lse2 = lse_log2(p.lse[ri]);
+      dl = p.delta[ri];
+    }
+  }
+  const float c = p.scale_log2;
+
+  f32x16_t acc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+
+  const unsigned short* Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hk * p.ks[2];
+  const unsigned short* Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hk * p.vs[2];
+  Stage<D> sk, sv;
+  if (T > 0) {
+    sk.load(Kg, p.ks[1], 0, k_hi, tid);
+    sv.load(Vg, p.vs[1], 0, k_hi, tid);
+    sk.store(kbuf[0], tid);
+    sv.store(vbuf[0], tid);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < T; ++t) {
+    const int cur = t & 1;
+    const bool more = t + 1 < T;
+    if (more) {
+      sk.load(Kg, p.ks[1], (t + 1) * 32, k_hi, tid);
+      sv.load(Vg, p.vs[1], (t + 1) * 32, k_hi, tid);
+    }
+    const char* kb = kbuf[cur];
+    const char* vb = vbuf[cur];
+    f32x16_t s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) s = Tt::mfma(frag_rows<D>(kb, l32, hi, kk), qf[kk], s);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) dp = Tt::mfma(frag_rows<D>(vb, l32, hi, kk), df[kk], dp);
+    // dS^T for this lane's row and its 16 keys (key of element r: k0 + (r/4)*8 + 4*hi + r%4).
+    const int k0 = t * 32;
+    u32x4_t dsb[2];
+#pragma unroll
+    for (int t16 = 0; t16 < 2; ++t16)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = 8 * t16 + 2 * e + u;
+          const int key = k0 + (r / 4) * 8 + hi * 4 + (r % 4);
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+          if (key >= k_hi || (CAUSAL && key > my_i + off)) pr = 0.f;
+          x[u] = pr * (dp[r] - dl);
+        }
+        dsb[t16][e] = Tt::pack2(x[0], x[1]);
+      }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int t16 = 0; t16 < 2; ++t16) acc[cb] = Tt::mfma(frag_cols<D>(kb, lane, hi, cb, t16), dsb[t16], acc[cb]);
+    if (more) {
+      sk.store(kbuf[cur ^ 1], tid);
+      sv.store(vbuf[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  if (row_ok) {
+    unsigned short* dst = (unsigned short*)p.dq + (int64_t)bb * p.dqs[0] + (int64_t)my_i * p.dqs[1] +
+                          (int64_t)hh * p.dqs[2];
+    store_cols<T_, D, CB>(dst, acc, hi, p.scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one work-group = 4 waves x 32 keys of one (b, K/V head); the query
+// rows of the g query heads that read the K/V head stream past in 32-row tiles.
+template <int T_, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
+  using Tt = Ty<T_>;
+  constexpr int KK = D / 16, CB = D >= 32 ? D / 32 : 1, BK = 128;
+  __shared__ __attribute__((aligned(16))) char qbuf[2][BTile<D>::BYTES];
+  __shared__ __attribute__((aligned(16))) char obuf[2][BTile<D>::BYTES];
+  __shared__ __attribute__((aligned(16))) float lbuf[2][32];
+  __shared__ __attribute__((aligned(16))) float dbuf[2][32];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h_kv = p.h / p.g;
+  const int per = p.b * h_kv;
+  const int kt = blockIdx.x / per;  // causal: low key tiles (seen by the most rows) first
+  const int bk = blockIdx.x - kt * per;
+  const int bb = bk / h_kv, hk = bk - bb * h_kv;
+  const int k0 = kt * BK;
+  const int my_j = k0 + wave * 32 + l32;
+  const bool key_ok = my_j < p.s_k;
+  const int off = p.s_k - p.s_q;
+  // Query rows that see any key of the block: i >= k0 - off when causal.
+  const int r_lo = CAUSAL ? max(0, k0 - off) : 0;
+  const int qt0 = r_lo / 32;
+  const int nq = r_lo < p.s_q ? (p.s_q + 31) / 32 - qt0 : 0;
+  const int T = p.g * nq;
+
+  // K and V of this lane's key: B operands of S = Q K^T and dP = dO V^T.
+  u32x4_t kf[KK], vf[KK];
+  {
+    const int j = min(my_j, p.s_k - 1);
+    const unsigned short* Kr = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)j * p.ks[1] +
+                               (int64_t)hk * p.ks[2];
+    const unsigned short* Vr = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)j * p.vs[1] +
+                               (int64_t)hk * p.vs[2];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      kf[kk] = *(const u32x4_t*)(Kr + hi * 8 + kk * 16);
+      vf[kk] = *(const u32x4_t*)(Vr + hi * 8 + kk * 16);
+    }
+  }
+  const float c = p.scale_log2;
+
+  f32x16_t dk[CB], dv[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[cb][r] = dv[cb][r] = 0.f;
+
+  Stage<D> sq, so;
+  float lr = INFINITY, dr = 0.f;  // threads 0..31: LSE (log2) and delta of one staged row
+  auto load_tile = [&](int t) {
+    const int hh = hk * p.g + t / nq;
+    const int q0 = (qt0 + t % nq) * 32;
+    const unsigned short* Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
+    const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2];
+    sq.load(Qg, p.qs[1], q0, p.s_q, tid);
+    so.load(Og, p.dos[1], q0, p.s_q, tid);
+    lr = INFINITY;
+    dr = 0.f;
+    if (tid < 32 && q0 + tid < p.s_q) {
+      const int64_t ri = ((int64_t)bb * p.h + hh) * p.s_q + q0 + tid;
+      lr = lse_log2(p.lse[ri]);
+      dr = p.delta[ri];
+    }
+  };
+  auto store_tile = [&](int buf) {
+    sq.store(qbuf[buf], tid);
+    so.store(obuf[buf], tid);
+    if (tid < 32) {
+      lbuf[buf][tid] = lr;
+      dbuf[buf][tid] = dr;
+    }
+  };
+  if (T > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < T; ++t) {
+    const int cur = t & 1;
+    const bool more = t + 1 < T;
+    if (more) load_tile(t + 1);
+    const int q0 = (qt0 + t % nq) * 32;
+    const char* qb = qbuf[cur];
+    const char* ob = obuf[cur];
+    f32x16_t s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) s = Tt::mfma(frag_rows<D>(qb, l32, hi, kk), kf[kk], s);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) dp = Tt::mfma(frag_rows<D>(ob, l32, hi, kk), vf[kk], dp);
+    // P and dS for this lane's key and its 16 rows (row of element r: q0 + (r/4)*8 + 4*hi + r%4).
+    u32x4_t pb[2], db[2];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4_t l4 = *(const f32x4_t*)(&lbuf[cur][r4 * 8 + hi * 4]);
+      const f32x4_t d4 = *(const f32x4_t*)(&dbuf[cur][r4 * 8 + hi * 4]);
+      float pr[4], ds[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * r4 + u;
+        const int row = q0 + r4 * 8 + hi * 4 + u;
+        float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l4[u]));
+        if (CAUSAL && my_j > row + off) x = 0.f;
+        pr[u] = x;
+        ds[u] = x * (dp[r] - d4[u]);
+      }
+      // elements 8*t16 .. 8*t16 + 7 form B-operand chunk t16
+      pb[r4 / 2][2 * (r4 % 2)] = Tt::pack2(pr[0], pr[1]);
+      pb[r4 / 2][2 * (r4 % 2) + 1] = Tt::pack2(pr[2], pr[3]);
+      db[r4 / 2][2 * (r4 % 2)] = Tt::pack2(ds[0], ds[1]);
+      db[r4 / 2][2 * (r4 % 2) + 1] = Tt::pack2(ds[2], ds[3]);
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int t16 = 0; t16 < 2; ++t16) {
+        dv[cb] = Tt::mfma(frag_cols<D>(ob, lane, hi, cb, t16), pb[t16], dv[cb]);
+        dk[cb] = Tt::mfma(frag_cols<D>(qb, lane, hi, cb, t16), db[t16], dk[cb]);
+      }
+    if (more) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (key_ok) {
+    unsigned short* dkp = (unsigned short*)p.dk + (int64_t)bb * p.dks[0] + (int64_t)my_j * p.dks[1] +
+                          (int64_t)hk * p.dks[2];
+    unsigned short* dvp = (unsigned short*)p.dv + (int64_t)bb * p.dvs[0] + (int64_t)my_j * p.dvs[1] +
+                          (int64_t)hk * p.dvs[2];
+    store_cols<T_, D, CB>(dkp, dk, hi, p.scale);
+    store_cols<T_, D, CB>(dvp, dv, hi, 1.f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers: delta, then the dQ and dK/dV kernels (both read delta), in order
+// on one stream.
+
+template <int T_, int D, bool CAUSAL>
+static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
+  const int64_t lanes = (int64_t)p.b * p.s_q * p.h * (D / 8);
+  hipLaunchKernelGGL((bwd_delta_kernel<T_, D>), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t g_dq = (int64_t)p.b * p.h * ((p.s_q + 127) / 128);
+  hipLaunchKernelGGL((bwd_dq_kernel<T_, D, CAUSAL>), dim3((unsigned)g_dq), dim3(256), 0, st, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t g_kv = (int64_t)p.b * (p.h / p.g) * ((p.s_k + 127) / 128);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T_, D, CAUSAL>), dim3((unsigned)g_kv), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int T_, bool CAUSAL>
+static hipError_t launch_bwd_c(const BwdParams& p, hipStream_t st) {
+  switch (p.d) {
+    case 16: return launch_bwd_t<T_, 16, CAUSAL>(p, st);
+    case 32: return launch_bwd_t<T_, 32, CAUSAL>(p, st);
+    case 64: return launch_bwd_t<T_, 64, CAUSAL>(p, st);
+    default: return launch_bwd_t<T_, 128, CAUSAL>(p, st);
+  }
+}
+
+hipError_t launch_bwd(const BwdParams& p, int dtype, bool causal, hipStream_t st) {
+  if (dtype == kBF16) return causal ? launch_bwd_c<kBF16, true>(p, st) : launch_bwd_c<kBF16, false>(p, st);
+  return causal ? launch_bwd_c<kFP16, true>(p, st) : launch_bwd_c<kFP16, false>(p, st);
+}
+
+}  // namespace attn

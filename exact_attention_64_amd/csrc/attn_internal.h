@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI front end (attn_api.cpp) and the gfx950
-// kernels (attn_fwd.hip, attn_decode.hip, attn_combine.hip).  Not installed; the public interface is attn.h.
+// kernels (attn_fwd.hip, attn_decode.hip, attn_combine.hip,
+// attn_bwd.hip).  Not installed; the public interface is attn.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -46,6 +47,26 @@ struct CombineParams {
   int64_t os[3];
   int b, h, s_q, d;
   int n_splits;
+};
+
+// Arguments of the backward kernels (attn_bwd.hip).  Strides are in elements,
+// for the (b, s, h) dimensions; d is contiguous.
+struct BwdParams {
+  const void* q;     // (b, s_q, h, d)
+  const void* k;     // (b, s_k, h / g, d)
+  const void* v;
+  const void* o;     // forward output (b, s_q, h, d)
+  const void* dout;  // upstream gradient of O (b, s_q, h, d)
+  const float* lse;  // forward LSE, dense (b, h, s_q), natural log
+  float* delta;      // dense (b, h, s_q): row dot of dO and O, written first
+  void* dq;          // (b, s_q, h, d), written
+  void* dk;          // (b, s_k, h / g, d), written
+  void* dv;
+  int64_t qs[3], ks[3], vs[3], os[3], dos[3], dqs[3], dks[3], dvs[3];
+  int b, h, s_q, s_k, d;
+  int g;             // query heads per K/V head
+  float scale;       // softmax scale (any finite value)
+  float scale_log2;  // scale * log2(e)
 };
 
 // Compile-time tunables (overridable with -D for sweeps).
@@ -122,5 +143,7 @@ inline hipError_t launch_fwd(const FwdParams& p, int dtype, bool causal, bool sp
                                                      : launch_prefill(p, dtype, causal, split, st);
 }
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t st);
+// Backward: delta, then dQ and dK/dV, enqueued in that order on `st`.
+hipError_t launch_bwd(const BwdParams& p, int dtype, bool causal, hipStream_t st);
 
 }  // namespace attn

@@ -211,6 +211,42 @@ attn_status attn_fwd_splitkv_paged(const attn_paged_args *args, int32_t num_spli
 attn_status attn_num_splits_paged(int64_t b, int64_t h, int64_t h_kv, int64_t s_q,
                                   int64_t max_seqlen_k, int64_t d, int device, int32_t *n_out);
 
+/* Backward pass.  flash-attention issue #1335 ("2.6.3 is faster than 2.7.0 for
+ * flash-attn v2 CUDA fwd/bwd") times the backward of the forward above on its
+ * fp16, head-dim-16 workloads; the pages do not describe its algorithm.  What it
+ * computes is the gradient of the definition at the top of this file: for an
+ * upstream gradient dO of O (LSE receives no gradient), per batch entry and
+ * query head, with P the forward's softmax weights,
+ *   dV_j  = sum_i P_ij dO_i                      (summed over the query heads
+ *   dK_j  = scale * sum_i dS_ij q_i               that share K/V head j's head)
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dS_ij = P_ij (dO_i . v_j - delta_i),  delta_i = dO_i . O_i.
+ * P is recomputed tile by tile from Q, K and the forward's LSE, never stored.
+ * A query row that sees no key (LSE = -inf) contributes nothing and gets dQ = 0.
+ * Every argument follows the rules of attn_args (shapes, h_kv, head dims,
+ * alignment, strides, finite scale, gfx950 device); the tensors are:
+ *   q, o, dout, dq : (b, s_q, h, d);   k, v, dk, dv : (b, s_k, h_kv, d)
+ * each with its own (b, s, h) element strides.  o and lse must be the forward's
+ * outputs for the same q, k, v, scale and causal flag (o in the input dtype, lse
+ * as attn_fwd writes it).  dq, dk, dv are written in the input dtype, computed
+ * from fp32 accumulators in a fixed order (deterministic).  delta is a caller-
+ * provided workspace, dense fp32 (b, h, s_q), overwritten with delta_i.
+ * The result is enqueued on `stream` as three kernels (delta, dQ, dK/dV). */
+typedef struct {
+  int32_t dtype;        /* attn_dtype of every tensor below except lse, delta */
+  int32_t causal;
+  int64_t b, s_q, s_k, h, h_kv, d;   /* h_kv: 0 means h */
+  const void *q, *k, *v, *o, *dout;  /* device pointers */
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3], dout_stride[3];
+  const float *lse;     /* dense (b, h, s_q) fp32, from attn_fwd */
+  void *dq, *dk, *dv;   /* device pointers, written */
+  int64_t dq_stride[3], dk_stride[3], dv_stride[3];
+  float *delta;         /* workspace, dense (b, h, s_q) fp32, written */
+  float softmax_scale;
+} attn_bwd_args;
+
+attn_status attn_bwd(const attn_bwd_args *args, void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *attn_status_str(int32_t status);
 

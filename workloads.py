@@ -88,6 +88,14 @@ def make_qkv(b: int, s_q: int, s_k: int, h: int, d: int, dtype: str, seed: int =
     return q, k, v
 
 
+def make_dout(b: int, s_q: int, h: int, d: int, dtype: str, seed: int = 43):
+    """Draw an upstream gradient dO (b, s_q, h, d) for the backward pass: i.i.d.
+    N(0, 1) from its own CPU generator (seed 43, so it is independent of the
+    q, k, v drawn with seed 42), rounded to ``dtype``."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return torch.randn((b, s_q, h, d), generator=g, dtype=torch.float32).to(DTYPES[dtype])
+
+
 def make_paged(b: int, s_q: int, h: int, d: int, dtype: str, seqlens, block_size: int,
                h_kv: int = 0, seed: int = 42, spare_blocks: int = 3):
     """Draw a query and a paged K/V cache for per-sequence key counts ``seqlens``.
