@@ -12,7 +12,10 @@ decode launches, taken between one pair of events, with L2 and the 256 MB MALL
 flushed by a 512 MiB fill before each pass) is reported beside it.  Kernel
 durations come from HIP events recorded on the stream the kernels run on.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|decode]
+The backward pass (attn_bwd) is reported beside them under "backward": the
+long causal workload and issue #1335's two fp16 head-dim-16 workloads.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|decode|backward]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -155,13 +158,56 @@ def cpu_baseline(w, budget_s: float = 12.0):
     }
 
 
+def bench_backward(torch, ea, workloads, dev, E):
+    """attn_bwd (delta, dQ, dK/dV kernels) on the long causal workload and on the
+    two fp16 head-dim-16 workloads whose backward issue #1335 times.  Inputs,
+    the forward's O and LSE, dO and every output resident in HBM; one event pair
+    per call, caches flushed before each (outside the events); median, min and
+    mean.  Algorithmic work: 10*d flops per visible (query, key) pair (five
+    products of 2*d: S, dP, dV, dK, dQ; the dQ kernel's recomputation of S and dP
+    is not counted)."""
+    W = workloads.WORKLOADS
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    outd = {}
+    for name, iters in (("C5", 5), ("C2", 50), ("C1", 50)):
+        w = W[name]
+        q, k, v = (t.to(dev) for t in workloads.make_workload(w))
+        do = workloads.make_dout(w.b, w.s_q, w.h, w.d, w.dtype).to(dev)
+        O, L = ea.attn_fwd(q, k, v, w.scale, w.causal)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty((w.b, w.h, w.s_q), dtype=torch.float32, device=dev)
+        run = lambda: ea.attn_bwd(q, k, v, O, do, L, w.scale, w.causal, dq=dq, dk=dk, dv=dv,  # noqa: E731
+                                  delta=delta)
+        for _ in range(2):
+            run()
+        ts = []
+        for _ in range(iters):
+            flush.fill_(0.0)
+            a, b = E(), E()
+            a.record()
+            run()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ts.sort()
+        med = ts[len(ts) // 2]
+        fl = 10 * w.d * visible_pairs(w)
+        outd[name] = dict(workload="backward of " + w.note, ms=round(med, 4), ms_min=round(ts[0], 4),
+                          ms_mean=round(sum(ts) / len(ts), 4), calls=iters, flops_per_call=fl,
+                          tflops=round(fl / (med * 1e-3) / 1e12, 2),
+                          frac_mfma=round(fl / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+        del q, k, v, do, O, L, dq, dk, dv, delta
+    del flush
+    return outd
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward"], default="all")
     ap.add_argument("--no-small", action="store_true", help="skip the per-workload side table")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy five times (reference "
@@ -424,6 +470,13 @@ def main():
             out["roofline"] = rd
     if side:
         out["other_workloads"] = side
+    if args.only in ("all", "backward") and not args.no_small:
+        out["backward"] = bench_backward(torch, ea, workloads, dev, E)
+        if args.only == "backward":
+            bc5 = out["backward"]["C5"]
+            out.update(value=bc5["tflops"], unit="TFLOP/s", config={
+                "workload": "backward (attn_bwd) of the causal prefill bf16 b=1 s_q=s_k=16384 h=32 d=128",
+                "b": wp.b, "s_q": wp.s_q, "s_k": wp.s_k, "h": wp.h, "d": wp.d, "causal": True})
     if args.only == "all" and not args.no_small:
         out["device"] = device_facts(torch, dev)
     if not args.no_cpu and do_p:
