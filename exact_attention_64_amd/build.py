@@ -26,15 +26,11 @@ SOURCES = [("attn_api.cpp", "attn_api", []),
            ("attn_combine.hip", "attn_combine", []),
            ("attn_bwd.hip", "attn_bwd", [])]
 
-# Translation units whose MFMA accumulators may live in AGPRs: the dK/dV kernel
-# keeps two fp32 accumulator sets (dK^T, dV^T) next to its K and V operands,
-# more than the 256 VGPRs of a lane.
-AGPR_SOURCES = {"attn_bwd.hip"}
-
 # Packed fp32 VALU instructions are switched off for every HIP translation unit.
-# Outside AGPR_SOURCES, MFMA accumulators are kept in VGPRs (the forward
-# kernels' vector ALU works on the score tile the matrix core produces;
-# AGPR-held scores would cost a copy per element).
+# MFMA accumulators are kept in VGPRs: the vector ALU works on the score tiles
+# the matrix core produces, and AGPR-held scores would cost a copy per element
+# (left to itself, the compiler also moved the backward's dK/dV accumulators
+# between AGPRs and VGPRs on every step).
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
@@ -56,8 +52,7 @@ def build(verbose: bool = False) -> str:
     for src, name, extra in SOURCES:
         obj = os.path.join(HERE, "_build", name + ".o")
         os.makedirs(os.path.dirname(obj), exist_ok=True)
-        acc = [] if src in AGPR_SOURCES else VGPR_ACC_FLAGS
-        cmd = [cc, *HIP_FLAGS, *acc, *extra, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIP_FLAGS, *VGPR_ACC_FLAGS, *extra, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd.insert(1, "-x")
             cmd.insert(2, "hip")

@@ -221,6 +221,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
     sk.store(kbuf[0], tid);
     sv.store(vbuf[0], tid);
   }
+  // Every load issued so far (this lane's Q, dO, LSE, delta) lands here, on every
+  // path: a load still pending where the loop starts would make the compiler
+  // wait inside the loop for all loads, the next tile's included.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < T; ++t) {
@@ -235,10 +239,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
     f32x16_t s, dp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+    // the two product chains interleaved, so that one's latency hides the other's
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) s = Tt::mfma(frag_rows<D>(kb, l32, hi, kk), qf[kk], s);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) dp = Tt::mfma(frag_rows<D>(vb, l32, hi, kk), df[kk], dp);
+    for (int kk = 0; kk < KK; ++kk) {
+      s = Tt::mfma(frag_rows<D>(kb, l32, hi, kk), qf[kk], s);
+      dp = Tt::mfma(frag_rows<D>(vb, l32, hi, kk), df[kk], dp);
+    }
     // dS^T for this lane's row and its 16 keys (key of element r: k0 + (r/4)*8 + 4*hi + r%4).
     const int k0 = t * 32;
     u32x4_t dsb[2];
@@ -327,7 +333,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
     for (int r = 0; r < 16; ++r) dk[cb][r] = dv[cb][r] = 0.f;
 
   Stage<D> sq, so;
-  float lr = INFINITY, dr = 0.f;  // threads 0..31: LSE (log2) and delta of one staged row
+  // LSE and delta of staged row tid % 32, loaded by every lane without a branch
+  // (the row index is clamped) and converted only when stored, so that nothing
+  // waits for these loads before the step's products.
+  float lr = 0.f, dr = 0.f;
+  bool row_in = false;
   auto load_tile = [&](int t) {
     const int hh = hk * p.g + t / nq;
     const int q0 = (qt0 + t % nq) * 32;
@@ -335,26 +345,26 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
     const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2];
     sq.load(Qg, p.qs[1], q0, p.s_q, tid);
     so.load(Og, p.dos[1], q0, p.s_q, tid);
-    lr = INFINITY;
-    dr = 0.f;
-    if (tid < 32 && q0 + tid < p.s_q) {
-      const int64_t ri = ((int64_t)bb * p.h + hh) * p.s_q + q0 + tid;
-      lr = lse_log2(p.lse[ri]);
-      dr = p.delta[ri];
-    }
+    const int row = q0 + (tid & 31);
+    row_in = row < p.s_q;
+    const int64_t ri = ((int64_t)bb * p.h + hh) * p.s_q + min(row, p.s_q - 1);
+    lr = p.lse[ri];
+    dr = p.delta[ri];
   };
   auto store_tile = [&](int buf) {
     sq.store(qbuf[buf], tid);
     so.store(obuf[buf], tid);
     if (tid < 32) {
-      lbuf[buf][tid] = lr;
-      dbuf[buf][tid] = dr;
+      lbuf[buf][tid] = row_in ? lse_log2(lr) : INFINITY;
+      dbuf[buf][tid] = row_in ? dr : 0.f;
     }
   };
   if (T > 0) {
     load_tile(0);
     store_tile(0);
   }
+  // K, V and the first tile land here, on every path (see the dQ kernel).
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < T; ++t) {
@@ -368,9 +378,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) s = Tt::mfma(frag_rows<D>(qb, l32, hi, kk), kf[kk], s);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) dp = Tt::mfma(frag_rows<D>(ob, l32, hi, kk), vf[kk], dp);
+    for (int kk = 0; kk < KK; ++kk) {
+      s = Tt::mfma(frag_rows<D>(qb, l32, hi, kk), kf[kk], s);
+      dp = Tt::mfma(frag_rows<D>(ob, l32, hi, kk), vf[kk], dp);
+    }
     // P and dS for this lane's key and its 16 rows (row of element r: q0 + (r/4)*8 + 4*hi + r%4).
     u32x4_t pb[2], db[2];
 #pragma unroll
