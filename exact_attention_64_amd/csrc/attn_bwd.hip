@@ -19,12 +19,15 @@
 //                      tiles of 32 keys stream through LDS; S^T, dP^T and dS^T are
 //                      formed so that each lane owns one query row (the forward's
 //                      layout) and dQ^T += K^T dS^T accumulates in registers;
-//   bwd_dkdv_kernel  : one work-group per (b, K/V head, 128 keys); Q and dO tiles
+//   bwd_dkdv_kernel,
+//   bwd_dkdv1_kernel : one work-group per (b, K/V head, 128 keys); Q and dO tiles
 //                      of 32 rows (of every query head of the group) stream
 //                      through LDS; S, dP and dS are formed so that each lane owns
 //                      one key, and dV^T += dO^T P, dK^T += Q^T dS accumulate in
-//                      registers.  Query heads sharing a K/V head are summed in
-//                      the same work-group, in a fixed order.
+//                      registers (of two partner waves at d = 128, of one wave
+//                      at smaller head dims).  Query heads sharing a
+//                      K/V head are summed in the same work-group, in a fixed
+//                      order.
 // Every product runs on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulation;
 // P and dS are rounded to the input type before they feed a product.
 #include "attn_common.h"
@@ -32,26 +35,43 @@
 namespace attn {
 namespace {
 
-// A 32-row tile of D elements in LDS, rows padded by 16 bytes so that a column
-// of 16-byte chunks read by 16 lanes falls on distinct banks.
+// A 32-row tile of D elements in LDS, 2*D bytes per row, its 16-byte chunks
+// XOR-swizzled per row (chunk c of row r sits at c ^ sw(r)) so that both read
+// patterns touch distinct banks (64 banks of 4 bytes):
+//  - row reads (ds_read_b128): 16 lanes read one chunk column of 16 rows;
+//  - transposed reads (ds_read_b64_tr_b16): 32 lanes read 64 bytes of each of 4
+//    rows r = 4m .. 4m + 3.
+// sw(r) takes distinct values over 16 consecutive rows that share a bank
+// position, and for D >= 64 moves the 4 rows of a transposed read to disjoint
+// 64-byte bank groups.
 template <int D> struct BTile {
-  static constexpr int RS = D * 2 + 16;  // bytes per row
+  static constexpr int RS = D * 2;       // bytes per row
   static constexpr int BYTES = 32 * RS;
   static constexpr int NCH = D / 8;      // 16-byte chunks per row
   static constexpr int CHUNKS = 32 * NCH;
-  static constexpr int NPT = (CHUNKS + 255) / 256;  // chunks per thread (256 threads)
+  static __device__ __forceinline__ int sw(int r) {
+    if constexpr (D == 128) return 4 * (r % 4) + (r / 4) % 4;
+    else if constexpr (D == 64) return 4 * ((r / 2) % 2) + (r / 4) % 4;
+    else if constexpr (D == 32) return (r / 4) % 4;
+    else return (r / 8) % 2;
+  }
+  // byte offset of element (r, col) (col a multiple of 4 here)
+  static __device__ __forceinline__ int at(int r, int col) {
+    return r * RS + 16 * ((col / 8) ^ sw(r)) + 2 * (col % 8);
+  }
 };
 
-// global -> registers -> LDS staging of one 32-row tile by the 256 threads of a
+// global -> registers -> LDS staging of one 32-row tile by the NTH threads of a
 // work-group.  Rows at or past `nrows` re-read row nrows - 1 (finite data; the
 // kernels mask or discard what those rows produce).
-template <int D> struct Stage {
-  u32x4_t r[BTile<D>::NPT];
+template <int D, int NTH = 256> struct Stage {
+  static constexpr int NPT = (BTile<D>::CHUNKS + NTH - 1) / NTH;  // chunks per thread
+  u32x4_t r[NPT];
   __device__ __forceinline__ void load(const unsigned short* __restrict__ G, int64_t rs, int row0, int nrows,
                                        int tid) {
 #pragma unroll
-    for (int i = 0; i < BTile<D>::NPT; ++i) {
-      const int c = tid + 256 * i;
+    for (int i = 0; i < NPT; ++i) {
+      const int c = tid + NTH * i;
       if (c < BTile<D>::CHUNKS) {
         const int row = min(row0 + c / BTile<D>::NCH, nrows - 1);
         r[i] = *(const u32x4_t*)(G + (int64_t)row * rs + (c % BTile<D>::NCH) * 8);
@@ -60,10 +80,10 @@ template <int D> struct Stage {
   }
   __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
-    for (int i = 0; i < BTile<D>::NPT; ++i) {
-      const int c = tid + 256 * i;
+    for (int i = 0; i < NPT; ++i) {
+      const int c = tid + NTH * i;
       if (c < BTile<D>::CHUNKS)
-        *(u32x4_t*)(lds + (c / BTile<D>::NCH) * BTile<D>::RS + (c % BTile<D>::NCH) * 16) = r[i];
+        *(u32x4_t*)(lds + BTile<D>::at(c / BTile<D>::NCH, (c % BTile<D>::NCH) * 8)) = r[i];
     }
   }
 };
@@ -73,7 +93,7 @@ template <int D> struct Stage {
 // product along D.
 template <int D>
 __device__ __forceinline__ u32x4_t frag_rows(const char* t, int l32, int hi, int kk) {
-  return *(const u32x4_t*)(t + l32 * BTile<D>::RS + 16 * (hi + 2 * kk));
+  return *(const u32x4_t*)(t + BTile<D>::at(l32, 8 * (hi + 2 * kk)));
 }
 
 // Transposed fragment of a 32-row LDS tile: the A operand of a product whose
@@ -93,7 +113,7 @@ __device__ __forceinline__ u32x4_t frag_cols(const char* t, int lane, int hi, in
 #pragma unroll
   for (int rd = 0; rd < 2; ++rd) {
     const int row = 16 * t16 + 8 * rd + 4 * hi + xr;
-    const char* a = t + row * BTile<D>::RS + col * 2;
+    const char* a = t + BTile<D>::at(row, col);
     const u32x2_t y = bitcast<u32x2_t>(__builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(a)));
     f[2 * rd] = y[0];
     f[2 * rd + 1] = y[1];
@@ -282,10 +302,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one work-group = 4 waves x 32 keys of one (b, K/V head); the query
-// rows of the g query heads that read the K/V head stream past in 32-row tiles.
+// dK, dV for d <= 64 (single-wave form): one work-group = 4 waves x 32 keys of
+// one (b, K/V head); each wave holds its keys' K and V and both accumulator sets
+// (few registers at these head dims), and computes S, dP, P, dS, dV^T and dK^T
+// itself, with one barrier per step.  The query rows of the g query heads that
+// read the K/V head stream past in 32-row tiles.
 template <int T_, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
+__global__ __launch_bounds__(256) void bwd_dkdv1_kernel(const BwdParams p) {
   using Tt = Ty<T_>;
   constexpr int KK = D / 16, CB = D >= 32 ? D / 32 : 1, BK = 128;
   __shared__ __attribute__((aligned(16))) char qbuf[2][BTile<D>::BYTES];
@@ -426,6 +449,166 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV for d = 128 (paired form): one work-group = 8 waves over 128 keys of one (b, K/V head); the query
+// rows of the g query heads that read the K/V head stream past in 32-row tiles.
+// The waves pair up per 32-key block kb (waves kb and kb + 4, which share a
+// SIMD):
+//   P-wave  (role 0): S = Q K^T, P = exp2(S*c - LSE*log2 e), hands P (fp32) to
+//                     its partner through LDS, and accumulates dV^T += dO^T P;
+//   dS-wave (role 1): dP = dO V^T, then, with the partner's P,
+//                     dS = P (dP - delta), and accumulates dK^T += Q^T dS.
+// So each wave holds one operand set (K or V of its keys) and one accumulator
+// set, two waves fit on a SIMD, and one wave's products overlap the other's
+// exponentials.  Per step: phase A (S or dP; the P-wave's exponentials and its
+// P handoff), a barrier, phase B (dV or dS and dK), the next tile's LDS stores,
+// a barrier.
+template <int T_, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
+  using Tt = Ty<T_>;
+  constexpr int KK = D / 16, CB = D >= 32 ? D / 32 : 1, BK = 128, NTH = 512;
+  __shared__ __attribute__((aligned(16))) char qbuf[2][BTile<D>::BYTES];
+  __shared__ __attribute__((aligned(16))) char obuf[2][BTile<D>::BYTES];
+  __shared__ __attribute__((aligned(16))) float lbuf[2][32];
+  __shared__ __attribute__((aligned(16))) float dbuf[2][32];
+  __shared__ __attribute__((aligned(16))) f32x4_t xbuf[4][4][64];  // [key block][r4][lane]: P
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = wave & 3, role = wave >> 2;
+  const int h_kv = p.h / p.g;
+  const int per = p.b * h_kv;
+  const int kt = blockIdx.x / per;  // causal: low key tiles (seen by the most rows) first
+  const int bk = blockIdx.x - kt * per;
+  const int bb = bk / h_kv, hk = bk - bb * h_kv;
+  const int k0 = kt * BK;
+  const int my_j = k0 + kb * 32 + l32;
+  const bool key_ok = my_j < p.s_k;
+  const int off = p.s_k - p.s_q;
+  // Query rows that see any key of the block: i >= k0 - off when causal.
+  const int r_lo = CAUSAL ? max(0, k0 - off) : 0;
+  const int qt0 = r_lo / 32;
+  const int nq = r_lo < p.s_q ? (p.s_q + 31) / 32 - qt0 : 0;
+  const int T = p.g * nq;
+
+  // This lane's key row of K (P-wave) or V (dS-wave): the B operand of
+  // S = Q K^T or dP = dO V^T.
+  u32x4_t opnd[KK];
+  {
+    const int j = min(my_j, p.s_k - 1);
+    const unsigned short* R =
+        role == 0 ? (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)j * p.ks[1] + (int64_t)hk * p.ks[2]
+                  : (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)j * p.vs[1] + (int64_t)hk * p.vs[2];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) opnd[kk] = *(const u32x4_t*)(R + hi * 8 + kk * 16);
+  }
+  const float c = p.scale_log2;
+
+  f32x16_t acc[CB];  // dV^T (P-wave) or dK^T (dS-wave)
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+
+  Stage<D, NTH> sq, so;
+  // LSE and delta of staged row tid % 32, loaded by every lane without a branch
+  // (the row index is clamped) and converted only when stored, so that nothing
+  // waits for these loads before the step's products.
+  float lr = 0.f, dr = 0.f;
+  bool row_in = false;
+  auto load_tile = [&](int t) {
+    const int hh = hk * p.g + t / nq;
+    const int q0 = (qt0 + t % nq) * 32;
+    const unsigned short* Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
+    const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2];
+    sq.load(Qg, p.qs[1], q0, p.s_q, tid);
+    so.load(Og, p.dos[1], q0, p.s_q, tid);
+    const int row = q0 + (tid & 31);
+    row_in = row < p.s_q;
+    const int64_t ri = ((int64_t)bb * p.h + hh) * p.s_q + min(row, p.s_q - 1);
+    lr = p.lse[ri];
+    dr = p.delta[ri];
+  };
+  auto store_tile = [&](int buf) {
+    sq.store(qbuf[buf], tid);
+    so.store(obuf[buf], tid);
+    if (tid < 32) {
+      lbuf[buf][tid] = row_in ? lse_log2(lr) : INFINITY;
+      dbuf[buf][tid] = row_in ? dr : 0.f;
+    }
+  };
+  if (T > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  // K or V and the first tile land here, on every path (see the dQ kernel).
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int t = 0; t < T; ++t) {
+    const int cur = t & 1;
+    const bool more = t + 1 < T;
+    if (more) load_tile(t + 1);
+    const int q0 = (qt0 + t % nq) * 32;
+    const char* qb = qbuf[cur];
+    const char* ob = obuf[cur];
+    // Phase A: S (P-wave) or dP (dS-wave) for this lane's key and its 16 rows
+    // (row of element r: q0 + (r/4)*8 + 4*hi + r%4).
+    f32x16_t sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+    const char* ab = role == 0 ? qb : ob;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) sc = Tt::mfma(frag_rows<D>(ab, l32, hi, kk), opnd[kk], sc);
+    u32x4_t bop[2];  // B operand of phase B: P (P-wave) or dS (dS-wave)
+    if (role == 0) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4_t l4 = *(const f32x4_t*)(&lbuf[cur][r4 * 8 + hi * 4]);
+        f32x4_t pr;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int row = q0 + r4 * 8 + hi * 4 + u;
+          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * r4 + u], c, -l4[u]));
+          if (CAUSAL && my_j > row + off) x = 0.f;
+          pr[u] = x;
+        }
+        xbuf[kb][r4][lane] = pr;
+        bop[r4 / 2][2 * (r4 % 2)] = Tt::pack2(pr[0], pr[1]);
+        bop[r4 / 2][2 * (r4 % 2) + 1] = Tt::pack2(pr[2], pr[3]);
+      }
+    }
+    __syncthreads();
+    // Phase B
+    if (role == 1) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4_t pr = xbuf[kb][r4][lane];
+        const f32x4_t d4 = *(const f32x4_t*)(&dbuf[cur][r4 * 8 + hi * 4]);
+        float ds[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ds[u] = pr[u] * (sc[4 * r4 + u] - d4[u]);
+        bop[r4 / 2][2 * (r4 % 2)] = Tt::pack2(ds[0], ds[1]);
+        bop[r4 / 2][2 * (r4 % 2) + 1] = Tt::pack2(ds[2], ds[3]);
+      }
+    }
+    const char* tb = role == 0 ? ob : qb;  // dO^T for dV, Q^T for dK
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int t16 = 0; t16 < 2; ++t16) acc[cb] = Tt::mfma(frag_cols<D>(tb, lane, hi, cb, t16), bop[t16], acc[cb]);
+    if (more) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (key_ok) {
+    unsigned short* dst =
+        role == 0 ? (unsigned short*)p.dv + (int64_t)bb * p.dvs[0] + (int64_t)my_j * p.dvs[1] + (int64_t)hk * p.dvs[2]
+                  : (unsigned short*)p.dk + (int64_t)bb * p.dks[0] + (int64_t)my_j * p.dks[1] + (int64_t)hk * p.dks[2];
+    store_cols<T_, D, CB>(dst, acc, hi, role == 0 ? 1.f : p.scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers: delta, then the dQ and dK/dV kernels (both read delta), in order
 // on one stream.
 
@@ -440,7 +623,13 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t g_kv = (int64_t)p.b * (p.h / p.g) * ((p.s_k + 127) / 128);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T_, D, CAUSAL>), dim3((unsigned)g_kv), dim3(256), 0, st, p);
+  // d = 128: paired waves (a single wave would need both operand and both
+  // accumulator sets, more than 256 registers); d <= 64: single-wave form
+  if constexpr (D == 128) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T_, D, CAUSAL>), dim3((unsigned)g_kv), dim3(512), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv1_kernel<T_, D, CAUSAL>), dim3((unsigned)g_kv), dim3(256), 0, st, p);
+  }
   return hipGetLastError();
 }
 
