@@ -449,28 +449,28 @@ __global__ __launch_bounds__(256) void bwd_dkdv1_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV for d = 128 (paired form): one work-group = 8 waves over 128 keys of one (b, K/V head); the query
-// rows of the g query heads that read the K/V head stream past in 32-row tiles.
-// The waves pair up per 32-key block kb (waves kb and kb + 4, which share a
-// SIMD):
+// dK, dV for d = 128 (paired form): one work-group = 8 waves over 128 keys of
+// one (b, K/V head); the query rows of the g query heads that read the K/V head
+// stream past in tiles of 64 rows (two 32-row halves).  The waves pair up per
+// 32-key block kb (waves kb and kb + 4, which share a SIMD):
 //   P-wave  (role 0): S = Q K^T, P = exp2(S*c - LSE*log2 e), hands P (fp32) to
 //                     its partner through LDS, and accumulates dV^T += dO^T P;
 //   dS-wave (role 1): dP = dO V^T, then, with the partner's P,
 //                     dS = P (dP - delta), and accumulates dK^T += Q^T dS.
 // So each wave holds one operand set (K or V of its keys) and one accumulator
 // set, two waves fit on a SIMD, and one wave's products overlap the other's
-// exponentials.  Per step: phase A (S or dP; the P-wave's exponentials and its
-// P handoff), a barrier, phase B (dV or dS and dK), the next tile's LDS stores,
-// a barrier.
+// exponentials.  Per step: phase A (S or dP of both halves, two independent
+// product chains; the P-wave's exponentials and its P handoff), a barrier,
+// phase B (dV or dS and dK), the next tile's LDS stores, a barrier.
 template <int T_, int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
   using Tt = Ty<T_>;
-  constexpr int KK = D / 16, CB = D >= 32 ? D / 32 : 1, BK = 128, NTH = 512;
-  __shared__ __attribute__((aligned(16))) char qbuf[2][BTile<D>::BYTES];
-  __shared__ __attribute__((aligned(16))) char obuf[2][BTile<D>::BYTES];
-  __shared__ __attribute__((aligned(16))) float lbuf[2][32];
-  __shared__ __attribute__((aligned(16))) float dbuf[2][32];
-  __shared__ __attribute__((aligned(16))) f32x4_t xbuf[4][4][64];  // [key block][r4][lane]: P
+  constexpr int KK = D / 16, CB = D >= 32 ? D / 32 : 1, BK = 128, NTH = 512, BQ = 64;
+  __shared__ __attribute__((aligned(16))) char qbuf[2][2][BTile<D>::BYTES];  // [buffer][half]
+  __shared__ __attribute__((aligned(16))) char obuf[2][2][BTile<D>::BYTES];
+  __shared__ __attribute__((aligned(16))) float lbuf[2][BQ];
+  __shared__ __attribute__((aligned(16))) float dbuf[2][BQ];
+  __shared__ __attribute__((aligned(16))) f32x4_t xbuf[2][4][4][64];  // [half][key block][r4][lane]: P
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -486,8 +486,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
   const int off = p.s_k - p.s_q;
   // Query rows that see any key of the block: i >= k0 - off when causal.
   const int r_lo = CAUSAL ? max(0, k0 - off) : 0;
-  const int qt0 = r_lo / 32;
-  const int nq = r_lo < p.s_q ? (p.s_q + 31) / 32 - qt0 : 0;
+  const int qt0 = r_lo / BQ;
+  const int nq = r_lo < p.s_q ? (p.s_q + BQ - 1) / BQ - qt0 : 0;
   const int T = p.g * nq;
 
   // This lane's key row of K (P-wave) or V (dS-wave): the B operand of
@@ -509,29 +509,35 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
-  Stage<D, NTH> sq, so;
-  // LSE and delta of staged row tid % 32, loaded by every lane without a branch
+  Stage<D, NTH> sq[2], so[2];
+  // LSE and delta of staged row tid % 64, loaded by every lane without a branch
   // (the row index is clamped) and converted only when stored, so that nothing
   // waits for these loads before the step's products.
   float lr = 0.f, dr = 0.f;
   bool row_in = false;
   auto load_tile = [&](int t) {
     const int hh = hk * p.g + t / nq;
-    const int q0 = (qt0 + t % nq) * 32;
+    const int q0 = (qt0 + t % nq) * BQ;
     const unsigned short* Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
     const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2];
-    sq.load(Qg, p.qs[1], q0, p.s_q, tid);
-    so.load(Og, p.dos[1], q0, p.s_q, tid);
-    const int row = q0 + (tid & 31);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      sq[hf].load(Qg, p.qs[1], q0 + 32 * hf, p.s_q, tid);
+      so[hf].load(Og, p.dos[1], q0 + 32 * hf, p.s_q, tid);
+    }
+    const int row = q0 + (tid & (BQ - 1));
     row_in = row < p.s_q;
     const int64_t ri = ((int64_t)bb * p.h + hh) * p.s_q + min(row, p.s_q - 1);
     lr = p.lse[ri];
     dr = p.delta[ri];
   };
   auto store_tile = [&](int buf) {
-    sq.store(qbuf[buf], tid);
-    so.store(obuf[buf], tid);
-    if (tid < 32) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      sq[hf].store(qbuf[buf][hf], tid);
+      so[hf].store(obuf[buf][hf], tid);
+    }
+    if (tid < BQ) {
       lbuf[buf][tid] = row_in ? lse_log2(lr) : INFINITY;
       dbuf[buf][tid] = row_in ? dr : 0.f;
     }
@@ -548,54 +554,65 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
     const int cur = t & 1;
     const bool more = t + 1 < T;
     if (more) load_tile(t + 1);
-    const int q0 = (qt0 + t % nq) * 32;
-    const char* qb = qbuf[cur];
-    const char* ob = obuf[cur];
-    // Phase A: S (P-wave) or dP (dS-wave) for this lane's key and its 16 rows
-    // (row of element r: q0 + (r/4)*8 + 4*hi + r%4).
-    f32x16_t sc;
+    const int q0 = (qt0 + t % nq) * BQ;
+    // Phase A: S (P-wave) or dP (dS-wave) of both halves for this lane's key and
+    // its 16 rows of each half (row of element r of half hf:
+    // q0 + 32*hf + (r/4)*8 + 4*hi + r%4).
+    f32x16_t sc[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-    const char* ab = role == 0 ? qb : ob;
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) sc = Tt::mfma(frag_rows<D>(ab, l32, hi, kk), opnd[kk], sc);
-    u32x4_t bop[2];  // B operand of phase B: P (P-wave) or dS (dS-wave)
+      for (int r = 0; r < 16; ++r) sc[hf][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        sc[hf] = Tt::mfma(frag_rows<D>(role == 0 ? qbuf[cur][hf] : obuf[cur][hf], l32, hi, kk), opnd[kk], sc[hf]);
+    u32x4_t bop[2][2];  // [half][chunk]: B operand of phase B, P (P-wave) or dS (dS-wave)
     if (role == 0) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4_t l4 = *(const f32x4_t*)(&lbuf[cur][r4 * 8 + hi * 4]);
-        f32x4_t pr;
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int row = q0 + r4 * 8 + hi * 4 + u;
-          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * r4 + u], c, -l4[u]));
-          if (CAUSAL && my_j > row + off) x = 0.f;
-          pr[u] = x;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4_t l4 = *(const f32x4_t*)(&lbuf[cur][32 * hf + r4 * 8 + hi * 4]);
+          f32x4_t pr;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int row = q0 + 32 * hf + r4 * 8 + hi * 4 + u;
+            float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hf][4 * r4 + u], c, -l4[u]));
+            if (CAUSAL && my_j > row + off) x = 0.f;
+            pr[u] = x;
+          }
+          xbuf[hf][kb][r4][lane] = pr;
+          bop[hf][r4 / 2][2 * (r4 % 2)] = Tt::pack2(pr[0], pr[1]);
+          bop[hf][r4 / 2][2 * (r4 % 2) + 1] = Tt::pack2(pr[2], pr[3]);
         }
-        xbuf[kb][r4][lane] = pr;
-        bop[r4 / 2][2 * (r4 % 2)] = Tt::pack2(pr[0], pr[1]);
-        bop[r4 / 2][2 * (r4 % 2) + 1] = Tt::pack2(pr[2], pr[3]);
-      }
     }
     __syncthreads();
     // Phase B
     if (role == 1) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4_t pr = xbuf[kb][r4][lane];
-        const f32x4_t d4 = *(const f32x4_t*)(&dbuf[cur][r4 * 8 + hi * 4]);
-        float ds[4];
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) ds[u] = pr[u] * (sc[4 * r4 + u] - d4[u]);
-        bop[r4 / 2][2 * (r4 % 2)] = Tt::pack2(ds[0], ds[1]);
-        bop[r4 / 2][2 * (r4 % 2) + 1] = Tt::pack2(ds[2], ds[3]);
-      }
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4_t pr = xbuf[hf][kb][r4][lane];
+          const f32x4_t d4 = *(const f32x4_t*)(&dbuf[cur][32 * hf + r4 * 8 + hi * 4]);
+          float ds[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) ds[u] = pr[u] * (sc[hf][4 * r4 + u] - d4[u]);
+          bop[hf][r4 / 2][2 * (r4 % 2)] = Tt::pack2(ds[0], ds[1]);
+          bop[hf][r4 / 2][2 * (r4 % 2) + 1] = Tt::pack2(ds[2], ds[3]);
+        }
     }
-    const char* tb = role == 0 ? ob : qb;  // dO^T for dV, Q^T for dK
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+    for (int hf = 0; hf < 2; ++hf) {
+      const char* tb = role == 0 ? obuf[cur][hf] : qbuf[cur][hf];  // dO^T for dV, Q^T for dK
 #pragma unroll
-      for (int t16 = 0; t16 < 2; ++t16) acc[cb] = Tt::mfma(frag_cols<D>(tb, lane, hi, cb, t16), bop[t16], acc[cb]);
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int t16 = 0; t16 < 2; ++t16)
+          acc[cb] = Tt::mfma(frag_cols<D>(tb, lane, hi, cb, t16), bop[hf][t16], acc[cb]);
+    }
     if (more) store_tile(cur ^ 1);
     __syncthreads();
   }
