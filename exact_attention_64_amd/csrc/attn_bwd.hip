@@ -139,6 +139,17 @@ __device__ __forceinline__ void store_cols(unsigned short* __restrict__ dst, con
     }
 }
 
+// Work-group id -> work item, XCD-aware.  Work-groups are dispatched to the
+// eight XCDs round-robin (id % 8), and each XCD has its own L2.  Item L =
+// xcd * q + min(xcd, r) + id / 8 (q, r = divmod(n, 8)) gives each XCD a
+// contiguous range of items, taken in order, so consecutive items (the blocks of
+// one head, which read the same K/V or Q/dO rows) share an XCD's L2.  A
+// bijection on [0, n) for every n.
+__device__ __forceinline__ int xcd_item(int id, int n) {
+  const int q = n / 8, r = n % 8, x = id % 8;
+  return x * q + min(x, r) + id / 8;
+}
+
 // log2-domain LSE of a row: +inf for a row that sees no key (LSE = -inf), so
 // that exp2(s*c - lse2) = 0 there.
 __device__ __forceinline__ float lse_log2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
@@ -191,10 +202,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_qt = (p.s_q + BM - 1) / BM;
-  const int per = p.b * p.h;
-  const int qt_rev = blockIdx.x / per;
-  const int bh = blockIdx.x - qt_rev * per;
-  const int qt = CAUSAL ? n_qt - 1 - qt_rev : qt_rev;  // causal: heaviest tiles first
+  // items (b*h, query tile) in head-major order, spread over the XCDs so that
+  // the tiles of a head share one L2; causal: heaviest tiles first
+  const int item = xcd_item(blockIdx.x, p.b * p.h * n_qt);
+  const int bh = item / n_qt;
+  const int qt_rev = item - bh * n_qt;
+  const int qt = CAUSAL ? n_qt - 1 - qt_rev : qt_rev;
   const int bb = bh / p.h, hh = bh - bb * p.h, hk = hh / p.g;
   const int q0 = qt * BM;
   const int my_i = q0 + wave * 32 + l32;
@@ -319,9 +332,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv1_kernel(const BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h_kv = p.h / p.g;
-  const int per = p.b * h_kv;
-  const int kt = blockIdx.x / per;  // causal: low key tiles (seen by the most rows) first
-  const int bk = blockIdx.x - kt * per;
+  const int n_kt = (p.s_k + BK - 1) / BK;
+  // items (b*h_kv, key block) in head-major order, spread over the XCDs so that
+  // the blocks of a head share one L2; causal: low key blocks (seen by the most
+  // rows) first
+  const int item = xcd_item(blockIdx.x, p.b * h_kv * n_kt);
+  const int bk = item / n_kt;
+  const int kt = item - bk * n_kt;
   const int bb = bk / h_kv, hk = bk - bb * h_kv;
   const int k0 = kt * BK;
   const int my_j = k0 + wave * 32 + l32;
@@ -363,7 +380,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv1_kernel(const BwdParams p) {
   bool row_in = false;
   auto load_tile = [&](int t) {
     const int hh = hk * p.g + t / nq;
-    const int q0 = (qt0 + t % nq) * 32;
+    const int q0 = (qt0 + nq - 1 - t % nq) * 32;  // last tile first
     const unsigned short* Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
     const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2];
     sq.load(Qg, p.qs[1], q0, p.s_q, tid);
@@ -394,7 +411,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv1_kernel(const BwdParams p) {
     const int cur = t & 1;
     const bool more = t + 1 < T;
     if (more) load_tile(t + 1);
-    const int q0 = (qt0 + t % nq) * 32;
+    const int q0 = (qt0 + nq - 1 - t % nq) * 32;  // last tile first
     const char* qb = qbuf[cur];
     const char* ob = obuf[cur];
     f32x16_t s, dp;
@@ -476,9 +493,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = wave & 3, role = wave >> 2;
   const int h_kv = p.h / p.g;
-  const int per = p.b * h_kv;
-  const int kt = blockIdx.x / per;  // causal: low key tiles (seen by the most rows) first
-  const int bk = blockIdx.x - kt * per;
+  const int n_kt = (p.s_k + BK - 1) / BK;
+  // items (b*h_kv, key block) in head-major order, spread over the XCDs so that
+  // the blocks of a head share one L2; causal: low key blocks (seen by the most
+  // rows) first
+  const int item = xcd_item(blockIdx.x, p.b * h_kv * n_kt);
+  const int bk = item / n_kt;
+  const int kt = item - bk * n_kt;
   const int bb = bk / h_kv, hk = bk - bb * h_kv;
   const int k0 = kt * BK;
   const int my_j = k0 + kb * 32 + l32;
@@ -517,7 +538,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
   bool row_in = false;
   auto load_tile = [&](int t) {
     const int hh = hk * p.g + t / nq;
-    const int q0 = (qt0 + t % nq) * BQ;
+    const int q0 = (qt0 + nq - 1 - t % nq) * BQ;  // last tile first
     const unsigned short* Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
     const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2];
 #pragma unroll
@@ -554,7 +575,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
     const int cur = t & 1;
     const bool more = t + 1 < T;
     if (more) load_tile(t + 1);
-    const int q0 = (qt0 + t % nq) * BQ;
+    const int q0 = (qt0 + nq - 1 - t % nq) * BQ;  // last tile first
     // Phase A: S (P-wave) or dP (dS-wave) of both halves for this lane's key and
     // its 16 rows of each half (row of element r of half hf:
     // q0 + 32*hf + (r/4)*8 + 4*hi + r%4).
