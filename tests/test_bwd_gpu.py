@@ -79,6 +79,8 @@ SMALL = [
     ("bf16", 1, 100, 90, 2, 2, 128),   # causal: the first rows see no key
     ("fp16", 1, 33, 300, 6, 2, 64),    # few rows, many keys, shared K/V heads
     ("bf16", 1, 1, 129, 2, 2, 128),    # one query row
+    ("bf16", 2, 200, 300, 8, 2, 128),  # d = 128 with four query heads per K/V head
+    ("fp16", 1, 257, 131, 6, 3, 128),  # the same in fp16, fewer keys than rows
 ]
 
 
@@ -180,3 +182,44 @@ def test_bwd_long_causal_sampled():
     assert np.abs(sv - want).max() <= 2e-2 * np.abs(want).max()
     sk = f64(dk).sum(axis=1)
     assert np.abs(sk).max() <= 2e-2 * np.abs(f64(dk)).sum(axis=1).max()
+
+
+def test_bwd_graph_capture_replay():
+    """attn_bwd enqueues kernels only, so a HIP graph can capture a forward +
+    backward pair; each replay (new inputs copied in, eager work between
+    replays) must equal an eager call bit for bit, and the first and last
+    replays match the oracle."""
+    say("HIP graph capture: attn_fwd + attn_bwd")
+    shape = (2, 150, 150, 4, 64)
+    b, s_q, s_k, h, d = shape
+    q, k, v = (t.to(DEV) for t in workloads.make_qkv(b, s_q, s_k, h, d, "bf16", seed=90, h_kv=2))
+    do = workloads.make_dout(b, s_q, h, d, "bf16", seed=91).to(DEV)
+    O = torch.empty_like(q)
+    L = torch.empty((b, h, s_q), device=DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((b, h, s_q), device=DEV)
+
+    def run(o, l, gq, gk, gv, dl):
+        ea.attn_fwd(q, k, v, 0.125, True, out=o, lse=l)
+        ea.attn_bwd(q, k, v, o, do, l, 0.125, True, dq=gq, dk=gk, dv=gv, delta=dl)
+
+    run(O, L, dq, dk, dv, delta)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(O, L, dq, dk, dv, delta)
+    E = [torch.empty_like(t) for t in (O, L, dq, dk, dv, delta)]
+    for rep in range(3):
+        new = workloads.make_qkv(b, s_q, s_k, h, d, "bf16", seed=100 + rep, h_kv=2)
+        new_do = workloads.make_dout(b, s_q, h, d, "bf16", seed=110 + rep)
+        for dst, src in zip((q, k, v, do), (*new, new_do)):
+            dst.copy_(src.to(DEV))
+        g.replay()
+        torch.cuda.synchronize()
+        run(*E)
+        torch.cuda.synchronize()
+        for got, want in zip((O, L, dq, dk, dv), E[:5]):
+            assert torch.equal(got, want), f"replay {rep} differs from the eager call"
+        if rep in (0, 2):
+            ref = oracle.attention_bwd(*host64(*new, new_do), 0.125, True)
+            check_full(dq, dk, dv, ref, "bf16", f"graph replay {rep}")
