@@ -15,7 +15,8 @@
 //   dQ_i  = scale * sum_j dS_ij k_j,   dK_j = scale * sum_i dS_ij q_i
 // Three kernels, all deterministic (no atomics):
 //   bwd_delta_kernel : delta (b, h, s_q) fp32 = row dot of dO and O;
-//   bwd_dq_kernel    : one work-group per (b, query head, 128 query rows); K and V
+//   bwd_dq_kernel    : one work-group per (b, query head, 256 query rows at d = 128,
+//                      128 below); K and V
 //                      tiles of 32 keys stream through LDS; S^T, dP^T and dS^T are
 //                      formed so that each lane owns one query row (the forward's
 //                      layout) and dQ^T += K^T dS^T accumulates in registers;
@@ -31,6 +32,10 @@
 // Every product runs on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulation;
 // P and dS are rounded to the input type before they feed a product.
 #include "attn_common.h"
+
+#ifndef ATTN_BWD_DQ_NW
+#define ATTN_BWD_DQ_NW 8  // waves (32 query rows each) per work-group of the d = 128 dQ kernel
+#endif
 
 namespace attn {
 namespace {
@@ -192,10 +197,11 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // dQ: one work-group = 4 waves x 32 query rows of one (b, query head).
-template <int T_, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
+// NW waves of 32 query rows per work-group.
+template <int T_, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
   using Tt = Ty<T_>;
-  constexpr int KK = D / 16, CB = D >= 32 ? D / 32 : 1, BM = 128;
+  constexpr int KK = D / 16, CB = D >= 32 ? D / 32 : 1, BM = NW * 32, NTH = NW * 64;
   __shared__ __attribute__((aligned(16))) char kbuf[2][BTile<D>::BYTES];
   __shared__ __attribute__((aligned(16))) char vbuf[2][BTile<D>::BYTES];
 
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
 
   const unsigned short* Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hk * p.ks[2];
   const unsigned short* Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hk * p.vs[2];
-  Stage<D> sk, sv;
+  Stage<D, NTH> sk, sv;
   if (T > 0) {
     sk.load(Kg, p.ks[1], 0, k_hi, tid);
     sv.load(Vg, p.vs[1], 0, k_hi, tid);
@@ -656,8 +662,11 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL((bwd_delta_kernel<T_, D>), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t g_dq = (int64_t)p.b * p.h * ((p.s_q + 127) / 128);
-  hipLaunchKernelGGL((bwd_dq_kernel<T_, D, CAUSAL>), dim3((unsigned)g_dq), dim3(256), 0, st, p);
+  // d = 128: 8 waves (256 rows) share each K/V tile (measured 3-6% faster on the
+  // 16k causal backward than 4); smaller head dims keep 4 (8 measured 2% slower at d = 16)
+  constexpr int NWQ = D == 128 ? ATTN_BWD_DQ_NW : 4;
+  const int64_t g_dq = (int64_t)p.b * p.h * ((p.s_q + NWQ * 32 - 1) / (NWQ * 32));
+  hipLaunchKernelGGL((bwd_dq_kernel<T_, D, CAUSAL, NWQ>), dim3((unsigned)g_dq), dim3(NWQ * 64), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t g_kv = (int64_t)p.b * (p.h / p.g) * ((p.s_k + 127) / 128);
