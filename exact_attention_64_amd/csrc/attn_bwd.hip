@@ -144,17 +144,6 @@ __device__ __forceinline__ void store_cols(unsigned short* __restrict__ dst, con
     }
 }
 
-// Work-group id -> work item, XCD-aware.  Work-groups are dispatched to the
-// eight XCDs round-robin (id % 8), and each XCD has its own L2.  Item L =
-// xcd * q + min(xcd, r) + id / 8 (q, r = divmod(n, 8)) gives each XCD a
-// contiguous range of items, taken in order, so consecutive items (the blocks of
-// one head, which read the same K/V or Q/dO rows) share an XCD's L2.  A
-// bijection on [0, n) for every n.
-__device__ __forceinline__ int xcd_item(int id, int n) {
-  const int q = n / 8, r = n % 8, x = id % 8;
-  return x * q + min(x, r) + id / 8;
-}
-
 // log2-domain LSE of a row: +inf for a row that sees no key (LSE = -inf), so
 // that exp2(s*c - lse2) = 0 there.
 __device__ __forceinline__ float lse_log2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }

@@ -62,6 +62,18 @@ template <> struct Ty<kFP16> {
   }
 };
 
+// Work-group id -> work item, XCD-aware.  Work-groups are dispatched to the
+// eight XCDs round-robin (id % 8), and each XCD has its own L2.  Item L =
+// xcd * q + min(xcd, r) + id / 8 (q, r = divmod(n, 8)) gives each XCD a
+// contiguous range of items, taken in order, so consecutive items (the tiles of
+// one head, which read the same K/V or Q/dO rows; neighbouring heads, which share
+// cache lines at small head dims) share an XCD's L2.  A bijection on [0, n) for
+// every n.
+__device__ __forceinline__ int xcd_item(int id, int n) {
+  const int q = n / 8, r = n % 8, x = id % 8;
+  return x * q + min(x, r) + id / 8;
+}
+
 // s_waitcnt immediate (gfx9 encoding): vmcnt(n), lgkmcnt(0), expcnt untouched.
 constexpr int vmcnt_lgkm0(int n) { return (n & 0xF) | (((n >> 4) & 0x3) << 14) | (0x7 << 4); }
 
