@@ -81,6 +81,9 @@ SMALL = [
     ("bf16", 1, 1, 129, 2, 2, 128),    # one query row
     ("bf16", 2, 200, 300, 8, 2, 128),  # d = 128 with four query heads per K/V head
     ("fp16", 1, 257, 131, 6, 3, 128),  # the same in fp16, fewer keys than rows
+    ("fp16", 2, 37, 1, 3, 3, 64),      # one key (causal: only the last row sees it)
+    ("bf16", 1, 5, 3, 2, 1, 128),      # three keys, five rows, one K/V head
+    ("bf16", 3, 70, 390, 5, 5, 32),    # 45 dK/dV and 15 dQ work-groups: uneven over the 8 XCDs
 ]
 
 
