@@ -275,6 +275,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
     }
     // dS^T for this lane's row and its 16 keys (key of element r: k0 + (r/4)*8 + 4*hi + r%4).
     const int k0 = t * 32;
+    // masks only where a key of the tile is past the range or (causal) after the
+    // diagonal of the wave's first row; wave-uniform
+    const bool edge = k0 + 32 > k_hi || (CAUSAL && k0 + 31 > q0 + wave * 32 + off);
     u32x4_t dsb[2];
 #pragma unroll
     for (int t16 = 0; t16 < 2; ++t16)
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
           const int r = 8 * t16 + 2 * e + u;
           const int key = k0 + (r / 4) * 8 + hi * 4 + (r % 4);
           float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-          if (key >= k_hi || (CAUSAL && key > my_i + off)) pr = 0.f;
+          if (edge && (key >= k_hi || (CAUSAL && key > my_i + off))) pr = 0.f;
           x[u] = pr * (dp[r] - dl);
         }
         dsb[t16][e] = Tt::pack2(x[0], x[1]);
@@ -419,6 +422,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv1_kernel(const BwdParams p) {
     }
     // P and dS for this lane's key and its 16 rows (row of element r: q0 + (r/4)*8 + 4*hi + r%4).
     u32x4_t pb[2], db[2];
+    const bool diag = k0 + wave * 32 + 31 > q0 + off;  // causal mask needed (wave-uniform)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const f32x4_t l4 = *(const f32x4_t*)(&lbuf[cur][r4 * 8 + hi * 4]);
@@ -429,7 +433,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv1_kernel(const BwdParams p) {
         const int r = 4 * r4 + u;
         const int row = q0 + r4 * 8 + hi * 4 + u;
         float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l4[u]));
-        if (CAUSAL && my_j > row + off) x = 0.f;
+        if (CAUSAL && diag && my_j > row + off) x = 0.f;
         pr[u] = x;
         ds[u] = x * (dp[r] - d4[u]);
       }
@@ -585,6 +589,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
       for (int hf = 0; hf < 2; ++hf)
         sc[hf] = Tt::mfma(frag_rows<D>(role == 0 ? qbuf[cur][hf] : obuf[cur][hf], l32, hi, kk), opnd[kk], sc[hf]);
     u32x4_t bop[2][2];  // [half][chunk]: B operand of phase B, P (P-wave) or dS (dS-wave)
+    // causal mask only where the wave's last key is after the diagonal of the
+    // tile's first row; wave-uniform
+    const bool diag = k0 + kb * 32 + 31 > q0 + off;
     if (role == 0) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
@@ -596,7 +603,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
           for (int u = 0; u < 4; ++u) {
             const int row = q0 + 32 * hf + r4 * 8 + hi * 4 + u;
             float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hf][4 * r4 + u], c, -l4[u]));
-            if (CAUSAL && my_j > row + off) x = 0.f;
+            if (CAUSAL && diag && my_j > row + off) x = 0.f;
             pr[u] = x;
           }
           xbuf[hf][kb][r4][lane] = pr;
