@@ -581,13 +581,16 @@ static hipError_t launch_fwd_rows(const FwdParams& p, hipStream_t st) {
 
 template <int T_, int D, bool PAGED, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwd_d(const FwdParams& p, hipStream_t st) {
-  // d <= 32: 4 waves (128 query rows) per work-group and up to four waves per
-  // SIMD; the paged cache is served at d >= 64 only (the host rejects the rest)
+  // d <= 32: ATTN_SMALL_D_NW = 2 waves (64 query rows) per work-group and up to
+  // four waves per SIMD (a work-group there has few steps and its start-up
+  // latency dominates, so more, smaller work-groups win: b = 512, s = 150,
+  // h = 16 measured 103.6 us with 2 waves, 110 with 4, 115 with 1); the paged
+  // cache is served at d >= 64 only (the host rejects the rest)
   if constexpr (D >= 64) {
     return fwd_packed(p.g, p.s_q, D) ? launch_fwd_rows<T_, D, true, PAGED, CAUSAL, SPLIT>(p, st)
                                      : launch_fwd_rows<T_, D, false, PAGED, CAUSAL, SPLIT>(p, st);
   } else if constexpr (!PAGED) {
-    return launch_fwdp_t<T_, D, 4, false, false, false, CAUSAL, SPLIT>(p, st);
+    return launch_fwdp_t<T_, D, ATTN_SMALL_D_NW, false, false, false, CAUSAL, SPLIT>(p, st);
   } else {
     return hipErrorInvalidValue;
   }

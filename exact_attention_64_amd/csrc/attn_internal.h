@@ -96,6 +96,9 @@ constexpr int kPrefillNBUF = ATTN_PREFILL_NBUF;
 constexpr int kStreamQTiles = ATTN_STREAM_QTILES;
 constexpr int kDecodeHeads = ATTN_DECODE_HEADS;
 constexpr int kDecodeBatch = ATTN_DECODE_BATCH;
+#ifndef ATTN_SMALL_D_NW
+#define ATTN_SMALL_D_NW 2   // waves (32 query rows each) per work-group of the d <= 32 prefill kernel
+#endif
 
 // Query heads sharing a K/V head (g > 1) with few query rows: the prefill kernel
 // packs a K/V head's g * s_q query rows into its work-groups (d >= 64).
@@ -104,7 +107,7 @@ inline bool fwd_packed(int64_t g, int64_t s_q, int d) { return g > 1 && s_q <= 6
 // the decode kernel (s_q == 1) puts kDecodeHeads heads in one work-group; the
 // prefill kernel one (b, h, query row block) per work-group.
 inline int64_t fwd_groups_per_split(int64_t b, int64_t h, int64_t g, int64_t s_q, int d) {
-  const int64_t bm = d >= 64 ? kPrefillNW * 32 : 4 * 32;  // prefill rows per work-group
+  const int64_t bm = d >= 64 ? kPrefillNW * 32 : ATTN_SMALL_D_NW * 32;  // prefill rows per work-group
   if (fwd_packed(g, s_q, d)) return b * (h / g) * ((g * s_q + bm - 1) / bm);
   if (s_q == 1) return (b * h + kDecodeHeads - 1) / kDecodeHeads;
   return b * h * ((s_q + bm - 1) / bm);
