@@ -353,10 +353,11 @@ attn_status attn_bwd(const attn_bwd_args* a, void* stream) {
   if (a->h_kv < 0 || a->h_kv > a->h || (a->h_kv > 0 && a->h % a->h_kv != 0)) return ATTN_E_SHAPE;
   const int64_t g = a->h_kv > 0 ? a->h / a->h_kv : 1;
   if (!headdim_ok(a->d)) return ATTN_E_HEADDIM;
-  // grids: delta (d/8 lanes per (b, row, head), 256 per work-group), dQ (128
-  // query rows), dK/dV (128 keys); every one must fit a 32-bit grid dimension
+  // grids: delta (d/8 lanes per (b, row, head), 256 per work-group), dQ (64 to
+  // 256 query rows per work-group), dK/dV (64 or 128 keys); every one must fit a
+  // 32-bit grid dimension (checked with the smallest blocks, 64)
   if (ceil_div(a->b * a->s_q * a->h * (a->d / 8), 256) > 0x7fffffff ||
-      a->b * a->h * ceil_div(a->s_q, 128) > 0x7fffffff || a->b * (a->h / g) * ceil_div(a->s_k, 128) > 0x7fffffff)
+      a->b * a->h * ceil_div(a->s_q, 64) > 0x7fffffff || a->b * (a->h / g) * ceil_div(a->s_k, 64) > 0x7fffffff)
     return ATTN_E_SHAPE;
   const void* t16[] = {a->q, a->k, a->v, a->o, a->dout, a->dq, a->dk, a->dv};
   for (const void* t : t16)

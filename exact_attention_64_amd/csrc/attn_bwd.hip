@@ -33,6 +33,9 @@
 // P and dS are rounded to the input type before they feed a product.
 #include "attn_common.h"
 
+#ifndef ATTN_BWD_SMALL_NW
+#define ATTN_BWD_SMALL_NW 2  // waves per work-group of the dQ and dK/dV kernels at d <= 32
+#endif
 #ifndef ATTN_BWD_DQ_NW
 #define ATTN_BWD_DQ_NW 8  // waves (32 query rows each) per work-group of the d = 128 dQ kernel
 #endif
@@ -318,10 +321,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
 // (few registers at these head dims), and computes S, dP, P, dS, dV^T and dK^T
 // itself, with one barrier per step.  The query rows of the g query heads that
 // read the K/V head stream past in 32-row tiles.
-template <int T_, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv1_kernel(const BwdParams p) {
+template <int T_, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv1_kernel(const BwdParams p) {
   using Tt = Ty<T_>;
-  constexpr int KK = D / 16, CB = D >= 32 ? D / 32 : 1, BK = 128;
+  constexpr int KK = D / 16, CB = D >= 32 ? D / 32 : 1, BK = NW * 32;
   __shared__ __attribute__((aligned(16))) char qbuf[2][BTile<D>::BYTES];
   __shared__ __attribute__((aligned(16))) char obuf[2][BTile<D>::BYTES];
   __shared__ __attribute__((aligned(16))) float lbuf[2][32];
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv1_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[cb][r] = dv[cb][r] = 0.f;
 
-  Stage<D> sq, so;
+  Stage<D, NW * 64> sq, so;
   // LSE and delta of staged row tid % 32, loaded by every lane without a branch
   // (the row index is clamped) and converted only when stored, so that nothing
   // waits for these loads before the step's products.
@@ -660,7 +663,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   if (e != hipSuccess) return e;
   // d = 128: 8 waves (256 rows) share each K/V tile (measured 3-6% faster on the
   // 16k causal backward than 4); smaller head dims keep 4 (8 measured 2% slower at d = 16)
-  constexpr int NWQ = D == 128 ? ATTN_BWD_DQ_NW : 4;
+  constexpr int NWQ = D == 128 ? ATTN_BWD_DQ_NW : (D <= 32 ? ATTN_BWD_SMALL_NW : 4);
   const int64_t g_dq = (int64_t)p.b * p.h * ((p.s_q + NWQ * 32 - 1) / (NWQ * 32));
   hipLaunchKernelGGL((bwd_dq_kernel<T_, D, CAUSAL, NWQ>), dim3((unsigned)g_dq), dim3(NWQ * 64), 0, st, p);
   e = hipGetLastError();
@@ -671,7 +674,9 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   if constexpr (D == 128) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T_, D, CAUSAL>), dim3((unsigned)g_kv), dim3(512), 0, st, p);
   } else {
-    hipLaunchKernelGGL((bwd_dkdv1_kernel<T_, D, CAUSAL>), dim3((unsigned)g_kv), dim3(256), 0, st, p);
+    constexpr int NWK = D <= 32 ? ATTN_BWD_SMALL_NW : 4;
+    const int64_t g1 = (int64_t)p.b * (p.h / p.g) * ((p.s_k + NWK * 32 - 1) / (NWK * 32));
+    hipLaunchKernelGGL((bwd_dkdv1_kernel<T_, D, CAUSAL, NWK>), dim3((unsigned)g1), dim3(NWK * 64), 0, st, p);
   }
   return hipGetLastError();
 }
