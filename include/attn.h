@@ -1,5 +1,5 @@
 /*
- * attn.h - exact attention forward for AMD MI355X (gfx950): the C ABI.
+ * attn.h - exact attention forward, flash-decoding and backward for AMD MI355X (gfx950): the C ABI.
  *
  * What is computed
  *   For every batch entry b, head h and query row i:
