@@ -13,11 +13,11 @@
 //   dP_ij = dO_i . v_j,   delta_i = dO_i . O_i
 //   dS_ij = P_ij (dP_ij - delta_i)
 //   dQ_i  = scale * sum_j dS_ij k_j,   dK_j = scale * sum_i dS_ij q_i
-// Three kernels, all deterministic (no atomics):
-//   bwd_delta_kernel : delta (b, h, s_q) fp32 = row dot of dO and O;
-//   bwd_dq_kernel    : one work-group per (b, query head, 256 query rows at d = 128,
-//                      128 below); K and V
-//                      tiles of 32 keys stream through LDS; S^T, dP^T and dS^T are
+// Two kernels, both deterministic (no atomics):
+//   bwd_dq_kernel    : one work-group per (b, query head, 32 to 256 query rows); it
+//                      also writes delta (b, h, s_q) fp32, the row dot of dO and O,
+//                      for the second kernel; K and V tiles of 32 keys stream
+//                      through LDS; S^T, dP^T and dS^T are
 //                      formed so that each lane owns one query row (the forward's
 //                      layout) and dQ^T += K^T dS^T accumulates in registers;
 //   bwd_dkdv_kernel,
@@ -155,40 +155,6 @@ __device__ __forceinline__ float lse_log2(float lse) { return lse == -INFINITY ?
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// delta_i = dO_i . O_i in fp32; D/8 lanes per (row, head), 16 bytes each.
-template <int T_, int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p) {
-  constexpr int NL = D / 8;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t pair = gid / NL;
-  const int part = (int)(gid % NL);
-  const int64_t total = (int64_t)p.b * p.s_q * p.h;
-  const bool ok = pair < total;
-  float acc = 0.f;
-  int hh = 0, i = 0, bb = 0;
-  if (ok) {
-    hh = (int)(pair % p.h);
-    const int64_t rest = pair / p.h;
-    i = (int)(rest % p.s_q);
-    bb = (int)(rest / p.s_q);
-    const u32x4_t a = *(const u32x4_t*)((const unsigned short*)p.dout + (int64_t)bb * p.dos[0] +
-                                         (int64_t)i * p.dos[1] + (int64_t)hh * p.dos[2] + part * 8);
-    const u32x4_t o = *(const u32x4_t*)((const unsigned short*)p.o + (int64_t)bb * p.os[0] +
-                                         (int64_t)i * p.os[1] + (int64_t)hh * p.os[2] + part * 8);
-    float fa[8], fo[8];
-    Dot<T_>::unpack8(a, fa);
-    Dot<T_>::unpack8(o, fo);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(fa[e], fo[e], acc);
-  }
-  // The NL lanes of a (row, head) are consecutive and NL divides 64, so a
-  // group never spans waves and is either wholly in range or wholly out.
-#pragma unroll
-  for (int m = NL / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 64);
-  if (ok && part == 0) p.delta[((int64_t)bb * p.h + hh) * p.s_q + i] = acc;
-}
-
-// ---------------------------------------------------------------------------
 // dQ: one work-group = 4 waves x 32 query rows of one (b, query head).
 // NW waves of 32 query rows per work-group.
 template <int T_, int D, bool CAUSAL, int NW>
@@ -224,16 +190,24 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
                                (int64_t)hh * p.qs[2];
     const unsigned short* Dr = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] +
                                (int64_t)my_i * p.dos[1] + (int64_t)hh * p.dos[2];
+    const unsigned short* Or = (const unsigned short*)p.o + (int64_t)bb * p.os[0] + (int64_t)my_i * p.os[1] +
+                               (int64_t)hh * p.os[2];
+    // delta = dO . O of this lane's row: each half-wave holds half of the row's
+    // columns (hi*8 + 16*kk), so the two halves meet in one lane swap
+    float part = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4_t z = {0u, 0u, 0u, 0u};
       qf[kk] = row_ok ? *(const u32x4_t*)(Qr + hi * 8 + kk * 16) : z;
       df[kk] = row_ok ? *(const u32x4_t*)(Dr + hi * 8 + kk * 16) : z;
+      const u32x4_t of = row_ok ? *(const u32x4_t*)(Or + hi * 8 + kk * 16) : z;
+      part = Dot<T_>::dot8(df[kk], of, part);
     }
+    dl = pair_sum(part);
     if (row_ok) {
       const int64_t ri = ((int64_t)bb * p.h + hh) * p.s_q + my_i;
       lse2 = lse_log2(p.lse[ri]);
-      dl = p.delta[ri];
+      if (hi == 0) p.delta[ri] = dl;  // for the dK/dV kernel, launched after this one
     }
   }
   const float c = p.scale_log2;
@@ -653,21 +627,17 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Launchers: delta, then the dQ and dK/dV kernels (both read delta), in order
-// on one stream.
+// Launchers: the dQ kernel (which also writes delta), then the dK/dV kernel
+// (which reads it), in order on one stream.
 
 template <int T_, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
-  const int64_t lanes = (int64_t)p.b * p.s_q * p.h * (D / 8);
-  hipLaunchKernelGGL((bwd_delta_kernel<T_, D>), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   // d = 128: 8 waves (256 rows) share each K/V tile (measured 3-6% faster on the
   // 16k causal backward than 4); smaller head dims keep 4 (8 measured 2% slower at d = 16)
   constexpr int NWQ = D == 128 ? ATTN_BWD_DQ_NW : (D <= 32 ? ATTN_BWD_SMALL_NW : 4);
   const int64_t g_dq = (int64_t)p.b * p.h * ((p.s_q + NWQ * 32 - 1) / (NWQ * 32));
   hipLaunchKernelGGL((bwd_dq_kernel<T_, D, CAUSAL, NWQ>), dim3((unsigned)g_dq), dim3(NWQ * 64), 0, st, p);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t g_kv = (int64_t)p.b * (p.h / p.g) * ((p.s_k + 127) / 128);
   // d = 128: paired waves (a single wave would need both operand and both

@@ -58,7 +58,7 @@ struct BwdParams {
   const void* o;     // forward output (b, s_q, h, d)
   const void* dout;  // upstream gradient of O (b, s_q, h, d)
   const float* lse;  // forward LSE, dense (b, h, s_q), natural log
-  float* delta;      // dense (b, h, s_q): row dot of dO and O, written first
+  float* delta;      // dense (b, h, s_q): row dot of dO and O, written by the dQ kernel
   void* dq;          // (b, s_q, h, d), written
   void* dk;          // (b, s_k, h / g, d), written
   void* dv;
@@ -146,7 +146,7 @@ inline hipError_t launch_fwd(const FwdParams& p, int dtype, bool causal, bool sp
                                                      : launch_prefill(p, dtype, causal, split, st);
 }
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t st);
-// Backward: delta, then dQ and dK/dV, enqueued in that order on `st`.
+// Backward: dQ (which also writes delta), then dK/dV, enqueued in that order on `st`.
 hipError_t launch_bwd(const BwdParams& p, int dtype, bool causal, hipStream_t st);
 
 }  // namespace attn

@@ -231,7 +231,8 @@ attn_status attn_num_splits_paged(int64_t b, int64_t h, int64_t h_kv, int64_t s_
  * as attn_fwd writes it).  dq, dk, dv are written in the input dtype, computed
  * from fp32 accumulators in a fixed order (deterministic).  delta is a caller-
  * provided workspace, dense fp32 (b, h, s_q), overwritten with delta_i.
- * The result is enqueued on `stream` as three kernels (delta, dQ, dK/dV). */
+ * The result is enqueued on `stream` as two kernels (dQ, which also writes
+ * delta, then dK/dV). */
 typedef struct {
   int32_t dtype;        /* attn_dtype of every tensor below except lse, delta */
   int32_t causal;
