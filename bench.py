@@ -341,12 +341,22 @@ def main():
                 ea.attn_fwd(q, k, v, w.scale, w.causal, out=O, lse=L)
             host_us = (time.perf_counter() - h0) / iters * 1e6
             torch.cuda.synchronize()
+            # the same call through a plan (arguments marshalled once)
+            plan = ea.FwdPlan(q, k, v, w.scale, w.causal, out=O, lse=L)
+            plan()
+            torch.cuda.synchronize()
+            h0 = time.perf_counter()
+            for _ in range(iters):
+                plan()
+            plan_host_us = (time.perf_counter() - h0) / iters * 1e6
+            torch.cuda.synchronize()
             ts.sort()
             med = ts[len(ts) // 2]
             io = 2 * w.b * w.h * w.d * (2 * w.s_q + 2 * w.s_k) + 4 * w.b * w.h * w.s_q
             side[name] = dict(workload=w.note, us=round(med * 1e3, 2), us_min=round(ts[0] * 1e3, 2),
                               us_mean=round(sum(ts) / len(ts) * 1e3, 2), launches=iters,
                               host_us_per_call=round(host_us, 2),
+                              host_us_per_call_plan=round(plan_host_us, 2),
                               tflops=round(flops(w) / (med * 1e-3) / 1e12, 2),
                               io_gbs=round(io / (med * 1e-3) / 1e9, 1),
                               frac_mfma=round(flops(w) / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))

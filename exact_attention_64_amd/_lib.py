@@ -210,6 +210,30 @@ def attn_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, stre
     return out, lse
 
 
+class FwdPlan:
+    """A fused-forward call with its arguments marshalled once: for callers that
+    run the same shapes and buffers repeatedly (issue #1335's point: at small
+    shapes host-side work per call is what costs time).  ``plan()`` only calls
+    the C ABI with the stored ``attn_args`` on the stored stream; the tensors
+    must stay alive and keep their storage (new values may be copied in)."""
+
+    def __init__(self, q, k, v, softmax_scale=None, causal=False, out=None, lse=None, stream=None):
+        b, s_q, h, d = q.shape
+        self.out = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+        self.lse = torch.empty((b, h, s_q), dtype=torch.float32, device=q.device) if lse is None else lse
+        self._keep = (q, k, v)
+        self._args = make_args(q, k, v, softmax_scale, causal, self.out, self.lse)
+        self._ref = ctypes.byref(self._args)
+        self._stream = _stream_ptr(q, stream)
+        self._fn = lib().attn_fwd
+
+    def __call__(self):
+        st = self._fn(self._ref, self._stream)
+        if st != 0:
+            _check(st)
+        return self.out, self.lse
+
+
 def attn_num_splits(b, h, s_q, s_k, d, device=None, h_kv=0) -> int:
     n = ctypes.c_int32(0)
     dev = torch.cuda.current_device() if device is None else int(device)

@@ -551,3 +551,22 @@ def test_bad_head_dim_rejected():
     with pytest.raises(ea.AttnError) as e:
         ea.attn_fwd(q, q, q)
     assert e.value.status == -4
+
+
+def test_forward_plan_matches_call():
+    """FwdPlan (arguments marshalled once) runs the same kernel: bit-identical to
+    attn_fwd, also after new values are copied into the planned inputs."""
+    say("FwdPlan vs attn_fwd")
+    q, k, v = upload(*workloads.make_qkv(2, 50, 50, 16, 16, "fp16", seed=71))
+    plan = ea.FwdPlan(q, k, v, 0.25, True)
+    O1, L1 = plan()
+    O2, L2 = ea.attn_fwd(q, k, v, 0.25, True)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+    new = workloads.make_qkv(2, 50, 50, 16, 16, "fp16", seed=72)
+    for dst, src in zip((q, k, v), new):
+        dst.copy_(src.to(DEV))
+    O1, L1 = plan()
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(*host64(*new), 0.25, True)
+    check(O1, L1, O_ref, L_ref, "fp16", "plan after new inputs")
