@@ -38,7 +38,7 @@ KERNEL_SOURCES = ["exact_attention_64_amd/csrc/attn_fwd.hip", "exact_attention_6
                   "exact_attention_64_amd/csrc/attn_combine.hip", "exact_attention_64_amd/csrc/attn_common.h",
                   "exact_attention_64_amd/csrc/attn_internal.h"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.md")
-CPU_ROWS_PER_HEAD = 2048  # seeded query rows per head in the CPU-baseline sample
+CPU_ROWS_PER_HEAD = 4096  # seeded query rows per head in the CPU-baseline sample (~12 s of oracle work)
 FLUSH_BYTES = 512 << 20   # written before each decode pass: evicts L2 and the 256 MB MALL
 
 
@@ -116,7 +116,7 @@ def device_facts(torch, dev):
             "copy_gbs": round(2 * n / (best * 1e-3) / 1e9, 1)}
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
+def cpu_baseline(w, budget_s: float = 20.0):
     """Time the float64 oracle on a bounded sample of the prefill workload: whole
     heads' worth of seeded query rows until about ``budget_s`` seconds of work."""
     import numpy as np
