@@ -97,8 +97,8 @@ def cpu_model() -> str:
 
 
 def device_facts(torch, dev):
-    """Compute-unit count, name and a measured copy bandwidth (1 GiB read + 1 GiB
-    written by torch's copy kernel, best of three) for context."""
+    """Compute-unit count, name, L2 size and a measured copy bandwidth (1 GiB read
+    + 1 GiB written by torch's copy kernel, best of four) for context."""
     props = torch.cuda.get_device_properties(dev)
     n = 1 << 30
     src = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -113,6 +113,7 @@ def device_facts(torch, dev):
         best = min(best, a.elapsed_time(b))
     del src, dst
     return {"name": getattr(props, "gcnArchName", props.name), "compute_units": props.multi_processor_count,
+            "l2_bytes": getattr(props, "L2_cache_size", None),
             "copy_gbs": round(2 * n / (best * 1e-3) / 1e9, 1)}
 
 
