@@ -155,8 +155,8 @@ __device__ __forceinline__ float lse_log2(float lse) { return lse == -INFINITY ?
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// dQ: one work-group = 4 waves x 32 query rows of one (b, query head).
-// NW waves of 32 query rows per work-group.
+// dQ: one work-group = NW waves x 32 query rows of one (b, query head) (8 waves
+// at d = 128, 4 at d = 64, one at d <= 32).
 template <int T_, int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
   using Tt = Ty<T_>;
