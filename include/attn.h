@@ -49,7 +49,9 @@
  *   keeps no pointer after a call returns, and enqueues kernels asynchronously
  *   on `stream` (a hipStream_t; NULL means the default stream).  Calls are
  *   thread-safe: the only state is a per-device cache of the compute-unit count
- *   and architecture, filled once.
+ *   and architecture, filled once.  Buffers a call writes (O, LSE, partials,
+ *   dQ, dK, dV, delta) must not overlap one another or any buffer the call
+ *   reads; this is not checked, and overlapping buffers give undefined results.
  *
  * Errors
  *   Every argument is checked on the host before anything is launched.  On any
