@@ -135,6 +135,35 @@ def test_bwd_strided_views():
     check_full(grads[:, :, :, 0], grads[:, :, :, 1], grads[:, :, :, 2], ref, "fp16", "strided")
 
 
+@pytest.mark.parametrize("d", [32, 128])
+def test_bwd_guard_bands_and_delta(d):
+    """Every output is written only inside its view (sentinels after each), and the
+    delta workspace holds rowsum(dO * O) of the O passed in."""
+    say("bwd guard bands, d", d)
+    b, s_q, s_k, h, h_kv = 1, 129, 77, 4, 2
+    q, k, v = workloads.make_qkv(b, s_q, s_k, h, d, "fp16", seed=21, h_kv=h_kv)
+    do = workloads.make_dout(b, s_q, h, d, "fp16", seed=22)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    O, L = ea.attn_fwd(qd, kd, vd, softmax_scale=0.2, causal=True)
+
+    def guarded(shape, dtype):
+        n = int(np.prod(shape))
+        full = torch.full((n + 4096,), 7.0, dtype=dtype, device=DEV)
+        return full, full[:n].view(shape)
+
+    bufs = [guarded(q.shape, torch.float16), guarded(k.shape, torch.float16),
+            guarded(v.shape, torch.float16), guarded((b, h, s_q), torch.float32)]
+    (_, dq), (_, dk), (_, dv), (_, delta) = bufs
+    ea.attn_bwd(qd, kd, vd, O, dod, L, softmax_scale=0.2, causal=True, dq=dq, dk=dk, dv=dv, delta=delta)
+    torch.cuda.synchronize()
+    for full, view in bufs:
+        assert (full[view.numel():] == 7.0).all()
+    ref = oracle.attention_bwd(*host64(q, k, v, do), 0.2, True)
+    check_full(dq, dk, dv, ref, "fp16", f"guard bands d={d}")
+    delta_host = np.einsum("bshd,bshd->bhs", f64(do), f64(O))
+    assert np.abs(f64(delta) - delta_host).max() <= 1e-4 * max(1.0, float(np.abs(delta_host).max()))
+
+
 def test_bwd_deterministic():
     say("bwd determinism")
     q, k, v = workloads.make_qkv(1, 300, 300, 4, 128, "bf16", seed=12, h_kv=2)
