@@ -17,13 +17,14 @@
 //   bwd_dq_kernel    : one work-group per (b, query head, 32 to 256 query rows); it
 //                      also writes delta (b, h, s_q) fp32, the row dot of dO and O,
 //                      for the second kernel; K and V tiles of 32 keys stream
-//                      through LDS; S^T, dP^T and dS^T are
+//                      into LDS by direct-to-LDS loads; S^T, dP^T and dS^T are
 //                      formed so that each lane owns one query row (the forward's
 //                      layout) and dQ^T += K^T dS^T accumulates in registers;
 //   bwd_dkdv_kernel,
 //   bwd_dkdv1_kernel : one work-group per (b, K/V head, 128 keys); Q and dO tiles
 //                      of 32 rows (of every query head of the group) stream
-//                      through LDS; S, dP and dS are formed so that each lane owns
+//                      through LDS (direct-to-LDS loads at d = 128, staged
+//                      through registers below); S, dP and dS are formed so that each lane owns
 //                      one key, and dV^T += dO^T P, dK^T += Q^T dS accumulate in
 //                      registers (of two partner waves at d = 128, of one wave
 //                      at smaller head dims).  Query heads sharing a
@@ -220,26 +221,35 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
 
   const unsigned short* Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hk * p.ks[2];
   const unsigned short* Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hk * p.vs[2];
-  Stage<D, NTH> sk, sv;
-  if (T > 0) {
-    sk.load(Kg, p.ks[1], 0, k_hi, tid);
-    sv.load(Vg, p.vs[1], 0, k_hi, tid);
-    sk.store(kbuf[0], tid);
-    sv.store(vbuf[0], tid);
-  }
-  // Every load issued so far (this lane's Q, dO, LSE, delta) lands here, on every
-  // path: a load still pending where the loop starts would make the compiler
-  // wait inside the loop for all loads, the next tile's included.
+  // K and V tiles go global -> LDS by direct-to-LDS loads: load i of wave w
+  // fills the 16-byte slots NTH*i + 64*w + lane of a tile, slot x being row
+  // x / NCH, physical chunk x % NCH, which receives the logical chunk the
+  // swizzle maps there.  Rows at or past k_hi re-read row k_hi - 1 (finite data,
+  // masked scores).
+  constexpr int NPT = BTile<D>::CHUNKS / NTH;
+  static_assert(BTile<D>::CHUNKS % NTH == 0, "whole tiles per load round");
+  auto issue = [&](int t, int buf) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int x = NTH * i + tid;
+      const int row = x / BTile<D>::NCH;
+      const int col = ((x % BTile<D>::NCH) ^ BTile<D>::sw(row)) * 8;
+      const int64_t r = min(t * 32 + row, k_hi - 1);
+      lds_dma16<false>(Kg + r * p.ks[1] + col, kbuf[buf] + (NTH * i + 64 * wave) * 16);
+      lds_dma16<false>(Vg + r * p.vs[1] + col, vbuf[buf] + (NTH * i + 64 * wave) * 16);
+    }
+  };
+  if (T > 0) issue(0, 0);
+  // Every load issued so far (this lane's Q, dO, O, LSE and the first tile)
+  // lands here, on every path: a load still pending where the loop starts would
+  // make the compiler wait inside the loop for all loads, the next tile's included.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < T; ++t) {
     const int cur = t & 1;
     const bool more = t + 1 < T;
-    if (more) {
-      sk.load(Kg, p.ks[1], (t + 1) * 32, k_hi, tid);
-      sv.load(Vg, p.vs[1], (t + 1) * 32, k_hi, tid);
-    }
+    if (more) issue(t + 1, cur ^ 1);  // that buffer was last read before the barrier ending step t - 1
     const char* kb = kbuf[cur];
     const char* vb = vbuf[cur];
     f32x16_t s, dp;
@@ -276,10 +286,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int t16 = 0; t16 < 2; ++t16) acc[cb] = Tt::mfma(frag_cols<D>(kb, lane, hi, cb, t16), dsb[t16], acc[cb]);
-    if (more) {
-      sk.store(kbuf[cur ^ 1], tid);
-      sv.store(vbuf[cur ^ 1], tid);
-    }
+    __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of tile t + 1 have landed
     __syncthreads();
   }
 
@@ -507,41 +514,44 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
-  Stage<D, NTH> sq[2], so[2];
+  // Q and dO tiles go global -> LDS by direct-to-LDS loads: wave w fills bytes
+  // [1024 w, 1024 w + 1024) of each 32-row tile, lane l the 16-byte slot
+  // 64 w + l, i.e. row (64 w + l) / NCH, physical chunk (64 w + l) % NCH, which
+  // receives the logical chunk the swizzle maps there.  Rows past s_q re-read
+  // row s_q - 1 (finite data; their LSE is +inf, so P = 0).
+  static_assert(BTile<D>::CHUNKS == NTH, "one 16-byte slot per thread and tile");
+  const int dma_row = tid / BTile<D>::NCH;
+  const int dma_col = ((tid % BTile<D>::NCH) ^ BTile<D>::sw(dma_row)) * 8;
   // LSE and delta of staged row tid % 64, loaded by every lane without a branch
   // (the row index is clamped) and converted only when stored, so that nothing
   // waits for these loads before the step's products.
   float lr = 0.f, dr = 0.f;
   bool row_in = false;
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](int t, int buf) {
     const int hh = hk * p.g + t / nq;
     const int q0 = (qt0 + nq - 1 - t % nq) * BQ;  // last tile first
-    const unsigned short* Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
-    const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      sq[hf].load(Qg, p.qs[1], q0 + 32 * hf, p.s_q, tid);
-      so[hf].load(Og, p.dos[1], q0 + 32 * hf, p.s_q, tid);
-    }
     const int row = q0 + (tid & (BQ - 1));
     row_in = row < p.s_q;
     const int64_t ri = ((int64_t)bb * p.h + hh) * p.s_q + min(row, p.s_q - 1);
     lr = p.lse[ri];
     dr = p.delta[ri];
-  };
-  auto store_tile = [&](int buf) {
+    const unsigned short* Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2] + dma_col;
+    const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2] + dma_col;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      sq[hf].store(qbuf[buf][hf], tid);
-      so[hf].store(obuf[buf][hf], tid);
+      const int64_t r = min(q0 + 32 * hf + dma_row, p.s_q - 1);
+      lds_dma16<false>(Qg + r * p.qs[1], qbuf[buf][hf] + wave * 1024);
+      lds_dma16<false>(Og + r * p.dos[1], obuf[buf][hf] + wave * 1024);
     }
+  };
+  auto store_tile = [&](int buf) {
     if (tid < BQ) {
       lbuf[buf][tid] = row_in ? lse_log2(lr) : INFINITY;
       dbuf[buf][tid] = row_in ? dr : 0.f;
     }
   };
   if (T > 0) {
-    load_tile(0);
+    load_tile(0, 0);
     store_tile(0);
   }
   // K or V and the first tile land here, on every path (see the dQ kernel).
@@ -551,7 +561,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
   for (int t = 0; t < T; ++t) {
     const int cur = t & 1;
     const bool more = t + 1 < T;
-    if (more) load_tile(t + 1);
+    if (more) load_tile(t + 1, cur ^ 1);  // that buffer was last read before the barrier ending step t - 1
     const int q0 = (qt0 + nq - 1 - t % nq) * BQ;  // last tile first
     // Phase A: S (P-wave) or dP (dS-wave) of both halves for this lane's key and
     // its 16 rows of each half (row of element r of half hf:
@@ -615,6 +625,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
           acc[cb] = Tt::mfma(frag_cols<D>(tb, lane, hi, cb, t16), bop[hf][t16], acc[cb]);
     }
     if (more) store_tile(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of tile t + 1 have landed
     __syncthreads();
   }
 

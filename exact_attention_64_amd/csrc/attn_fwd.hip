@@ -78,33 +78,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// One direct-to-LDS wave load: lane i copies 16 bytes from gptr to LDS byte
-// address lds + 16 i (lds is wave-uniform).  Written as inline asm so that the
-// compiler does not treat the LDS write as aliasing the reads of other ring
-// slots and wait for every load in flight before them (it cannot bound the
-// per-wave offset); the kernel orders these loads with its own s_waitcnt
-// vmcnt and barriers.  Loads complete in order, so the compiler's own vmcnt
-// waits for other loads stay correct.  The s_nop covers the M0 -> LDS DMA
-// hazard.  NT sets the nontemporal bit: a tile that no other work-group reads
-// should not allocate in the caches, where it would only push other lines out
-// (dirty ones at the cost of a write-back each; measured on gfx950, default-
-// policy streaming reads fall to about half the rate of nontemporal ones when
-// the last-level cache holds dirty lines, and run about 12% slower when clean).
-template <bool NT>
-__device__ __forceinline__ void lds_dma16(const void* gptr, const char* lds) {
-  const unsigned m0v = (unsigned)(uintptr_t)(const LDS_AS char*)lds;
-  if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
-                 :
-                 : "s"(m0v), "v"(gptr)
-                 : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(m0v), "v"(gptr)
-                 : "memory", "m0");
-}
-
 // PACK (query heads sharing a K/V head, few query rows): a work-group covers one
 // (batch, K/V head) and its g * s_q query rows, row r being query head
 // hk * g + r / s_q at position r % s_q, so every K/V tile serves the whole group.
