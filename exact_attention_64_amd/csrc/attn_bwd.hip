@@ -21,10 +21,10 @@
 //                      formed so that each lane owns one query row (the forward's
 //                      layout) and dQ^T += K^T dS^T accumulates in registers;
 //   bwd_dkdv_kernel,
-//   bwd_dkdv1_kernel : one work-group per (b, K/V head, 128 keys); Q and dO tiles
+//   bwd_dkdv1_kernel : one work-group per (b, K/V head, 32 to 128 keys); Q and dO tiles
 //                      of 32 rows (of every query head of the group) stream
-//                      through LDS (direct-to-LDS loads at d = 128, staged
-//                      through registers below); S, dP and dS are formed so that each lane owns
+//                      into LDS by direct-to-LDS loads; S, dP and dS are
+//                      formed so that each lane owns
 //                      one key, and dV^T += dO^T P, dK^T += Q^T dS accumulate in
 //                      registers (of two partner waves at d = 128, of one wave
 //                      at smaller head dims).  Query heads sharing a
@@ -71,32 +71,26 @@ template <int D> struct BTile {
   }
 };
 
-// global -> registers -> LDS staging of one 32-row tile by the NTH threads of a
-// work-group.  Rows at or past `nrows` re-read row nrows - 1 (finite data; the
-// kernels mask or discard what those rows produce).
-template <int D, int NTH = 256> struct Stage {
-  static constexpr int NPT = (BTile<D>::CHUNKS + NTH - 1) / NTH;  // chunks per thread
-  u32x4_t r[NPT];
-  __device__ __forceinline__ void load(const unsigned short* __restrict__ G, int64_t rs, int row0, int nrows,
-                                       int tid) {
+// global -> LDS copy of one 32-row tile by the NTH threads of a work-group with
+// direct-to-LDS loads: load i of wave w fills the 16-byte slots NTH*i + 64*w +
+// lane, slot x being row x / NCH, physical chunk x % NCH, which receives the
+// logical chunk the swizzle maps there.  Rows at or past `nrows` re-read row
+// nrows - 1 (finite data; the kernels mask or discard what those rows produce).
+// The caller waits for the loads (s_waitcnt) before the barrier that publishes
+// the tile.
+template <int D, int NTH>
+__device__ __forceinline__ void dma_tile(const unsigned short* __restrict__ G, int64_t rs, int row0, int nrows,
+                                         int tid, int wave, char* lds) {
+  static_assert(BTile<D>::CHUNKS % NTH == 0, "whole tiles per load round");
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int c = tid + NTH * i;
-      if (c < BTile<D>::CHUNKS) {
-        const int row = min(row0 + c / BTile<D>::NCH, nrows - 1);
-        r[i] = *(const u32x4_t*)(G + (int64_t)row * rs + (c % BTile<D>::NCH) * 8);
-      }
-    }
+  for (int i = 0; i < BTile<D>::CHUNKS / NTH; ++i) {
+    const int x = NTH * i + tid;
+    const int row = x / BTile<D>::NCH;
+    const int col = ((x % BTile<D>::NCH) ^ BTile<D>::sw(row)) * 8;
+    const int64_t r = min(row0 + row, nrows - 1);
+    lds_dma16<false>(G + r * rs + col, lds + (NTH * i + 64 * wave) * 16);
   }
-  __device__ __forceinline__ void store(char* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int c = tid + NTH * i;
-      if (c < BTile<D>::CHUNKS)
-        *(u32x4_t*)(lds + BTile<D>::at(c / BTile<D>::NCH, (c % BTile<D>::NCH) * 8)) = r[i];
-    }
-  }
-};
+}
 
 // Row-major fragment of a 32-row LDS tile: lane (l32, hi) gets elements
 // [8*hi + 16*kk, +8) of row l32, the A (or B) operand layout of the 32x32x16
@@ -221,23 +215,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
 
   const unsigned short* Kg = (const unsigned short*)p.k + (int64_t)bb * p.ks[0] + (int64_t)hk * p.ks[2];
   const unsigned short* Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hk * p.vs[2];
-  // K and V tiles go global -> LDS by direct-to-LDS loads: load i of wave w
-  // fills the 16-byte slots NTH*i + 64*w + lane of a tile, slot x being row
-  // x / NCH, physical chunk x % NCH, which receives the logical chunk the
-  // swizzle maps there.  Rows at or past k_hi re-read row k_hi - 1 (finite data,
-  // masked scores).
-  constexpr int NPT = BTile<D>::CHUNKS / NTH;
-  static_assert(BTile<D>::CHUNKS % NTH == 0, "whole tiles per load round");
+  // K and V tiles go global -> LDS by direct-to-LDS loads; rows at or past k_hi
+  // re-read row k_hi - 1 (finite data, masked scores)
   auto issue = [&](int t, int buf) {
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int x = NTH * i + tid;
-      const int row = x / BTile<D>::NCH;
-      const int col = ((x % BTile<D>::NCH) ^ BTile<D>::sw(row)) * 8;
-      const int64_t r = min(t * 32 + row, k_hi - 1);
-      lds_dma16<false>(Kg + r * p.ks[1] + col, kbuf[buf] + (NTH * i + 64 * wave) * 16);
-      lds_dma16<false>(Vg + r * p.vs[1] + col, vbuf[buf] + (NTH * i + 64 * wave) * 16);
-    }
+    dma_tile<D, NTH>(Kg, p.ks[1], t * 32, k_hi, tid, wave, kbuf[buf]);
+    dma_tile<D, NTH>(Vg, p.vs[1], t * 32, k_hi, tid, wave, vbuf[buf]);
   };
   if (T > 0) issue(0, 0);
   // Every load issued so far (this lane's Q, dO, O, LSE and the first tile)
@@ -355,35 +337,34 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv1_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[cb][r] = dv[cb][r] = 0.f;
 
-  Stage<D, NW * 64> sq, so;
+  // Q and dO tiles go global -> LDS by direct-to-LDS loads (rows past s_q re-read
+  // row s_q - 1: finite data, and their LSE is +inf, so P = 0).
   // LSE and delta of staged row tid % 32, loaded by every lane without a branch
   // (the row index is clamped) and converted only when stored, so that nothing
   // waits for these loads before the step's products.
   float lr = 0.f, dr = 0.f;
   bool row_in = false;
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](int t, int buf) {
     const int hh = hk * p.g + t / nq;
     const int q0 = (qt0 + nq - 1 - t % nq) * 32;  // last tile first
-    const unsigned short* Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
-    const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2];
-    sq.load(Qg, p.qs[1], q0, p.s_q, tid);
-    so.load(Og, p.dos[1], q0, p.s_q, tid);
     const int row = q0 + (tid & 31);
     row_in = row < p.s_q;
     const int64_t ri = ((int64_t)bb * p.h + hh) * p.s_q + min(row, p.s_q - 1);
     lr = p.lse[ri];
     dr = p.delta[ri];
+    const unsigned short* Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
+    const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2];
+    dma_tile<D, NW * 64>(Qg, p.qs[1], q0, p.s_q, tid, wave, qbuf[buf]);
+    dma_tile<D, NW * 64>(Og, p.dos[1], q0, p.s_q, tid, wave, obuf[buf]);
   };
   auto store_tile = [&](int buf) {
-    sq.store(qbuf[buf], tid);
-    so.store(obuf[buf], tid);
     if (tid < 32) {
       lbuf[buf][tid] = row_in ? lse_log2(lr) : INFINITY;
       dbuf[buf][tid] = row_in ? dr : 0.f;
     }
   };
   if (T > 0) {
-    load_tile(0);
+    load_tile(0, 0);
     store_tile(0);
   }
   // K, V and the first tile land here, on every path (see the dQ kernel).
@@ -393,7 +374,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv1_kernel(const BwdParams p) {
   for (int t = 0; t < T; ++t) {
     const int cur = t & 1;
     const bool more = t + 1 < T;
-    if (more) load_tile(t + 1);
+    if (more) load_tile(t + 1, cur ^ 1);  // that buffer was last read before the barrier ending step t - 1
     const int q0 = (qt0 + nq - 1 - t % nq) * 32;  // last tile first
     const char* qb = qbuf[cur];
     const char* ob = obuf[cur];
@@ -436,6 +417,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv1_kernel(const BwdParams p) {
         dk[cb] = Tt::mfma(frag_cols<D>(qb, lane, hi, cb, t16), db[t16], dk[cb]);
       }
     if (more) store_tile(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of tile t + 1 have landed
     __syncthreads();
   }
 
@@ -514,14 +496,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
-  // Q and dO tiles go global -> LDS by direct-to-LDS loads: wave w fills bytes
-  // [1024 w, 1024 w + 1024) of each 32-row tile, lane l the 16-byte slot
-  // 64 w + l, i.e. row (64 w + l) / NCH, physical chunk (64 w + l) % NCH, which
-  // receives the logical chunk the swizzle maps there.  Rows past s_q re-read
-  // row s_q - 1 (finite data; their LSE is +inf, so P = 0).
-  static_assert(BTile<D>::CHUNKS == NTH, "one 16-byte slot per thread and tile");
-  const int dma_row = tid / BTile<D>::NCH;
-  const int dma_col = ((tid % BTile<D>::NCH) ^ BTile<D>::sw(dma_row)) * 8;
+  // Q and dO tiles go global -> LDS by direct-to-LDS loads (rows past s_q re-read
+  // row s_q - 1: finite data, and their LSE is +inf, so P = 0).
   // LSE and delta of staged row tid % 64, loaded by every lane without a branch
   // (the row index is clamped) and converted only when stored, so that nothing
   // waits for these loads before the step's products.
@@ -535,13 +511,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
     const int64_t ri = ((int64_t)bb * p.h + hh) * p.s_q + min(row, p.s_q - 1);
     lr = p.lse[ri];
     dr = p.delta[ri];
-    const unsigned short* Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2] + dma_col;
-    const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2] + dma_col;
+    const unsigned short* Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
+    const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const int64_t r = min(q0 + 32 * hf + dma_row, p.s_q - 1);
-      lds_dma16<false>(Qg + r * p.qs[1], qbuf[buf][hf] + wave * 1024);
-      lds_dma16<false>(Og + r * p.dos[1], obuf[buf][hf] + wave * 1024);
+      dma_tile<D, NTH>(Qg, p.qs[1], q0 + 32 * hf, p.s_q, tid, wave, qbuf[buf][hf]);
+      dma_tile<D, NTH>(Og, p.dos[1], q0 + 32 * hf, p.s_q, tid, wave, obuf[buf][hf]);
     }
   };
   auto store_tile = [&](int buf) {
