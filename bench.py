@@ -197,6 +197,19 @@ def bench_backward(torch, ea, workloads, dev, E):
                           ms_mean=round(sum(ts) / len(ts), 4), calls=iters, flops_per_call=fl,
                           tflops=round(fl / (med * 1e-3) / 1e12, 2),
                           frac_mfma=round(fl / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+        if name == "C1":
+            # host time per call at the tiny shape (issue #1335's subject): through
+            # the binding, and through a plan with the arguments marshalled once
+            plan = ea.BwdPlan(q, k, v, O, do, L, w.scale, w.causal, dq=dq, dk=dk, dv=dv, delta=delta)
+            for key, fn in (("host_us_per_call", run), ("host_us_per_call_plan", plan)):
+                fn()
+                torch.cuda.synchronize()
+                h0 = time.perf_counter()
+                for _ in range(200):
+                    fn()
+                outd[name][key] = round((time.perf_counter() - h0) / 200 * 1e6, 2)
+                torch.cuda.synchronize()
+            del plan
         del q, k, v, do, O, L, dq, dk, dv, delta
     del flush
     return outd

@@ -452,3 +452,30 @@ def attn_bwd(q, k, v, out, dout, lse, softmax_scale=None, causal=False, dq=None,
     a = make_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, delta, softmax_scale, causal)
     _check(lib().attn_bwd(ctypes.byref(a), _stream_ptr(q, stream)))
     return dq, dk, dv
+
+
+class BwdPlan:
+    """A backward call with its arguments marshalled once, like FwdPlan: ``plan()``
+    only calls the C ABI with the stored ``attn_bwd_args`` on the stored stream;
+    the tensors must stay alive and keep their storage (new values may be
+    copied in).  Returns (dq, dk, dv)."""
+
+    def __init__(self, q, k, v, out, dout, lse, softmax_scale=None, causal=False, dq=None, dk=None, dv=None,
+                 delta=None, stream=None):
+        b, s_q, h, d = q.shape
+        self.dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+        self.dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+        self.dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+        self.delta = torch.empty((b, h, s_q), dtype=torch.float32, device=q.device) if delta is None else delta
+        self._keep = (q, k, v, out, dout, lse)
+        self._args = make_bwd_args(q, k, v, out, dout, lse, self.dq, self.dk, self.dv, self.delta,
+                                   softmax_scale, causal)
+        self._ref = ctypes.byref(self._args)
+        self._stream = _stream_ptr(q, stream)
+        self._fn = lib().attn_bwd
+
+    def __call__(self):
+        st = self._fn(self._ref, self._stream)
+        if st != 0:
+            _check(st)
+        return self.dq, self.dk, self.dv

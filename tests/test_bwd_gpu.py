@@ -164,6 +164,28 @@ def test_bwd_guard_bands_and_delta(d):
     assert np.abs(f64(delta) - delta_host).max() <= 1e-4 * max(1.0, float(np.abs(delta_host).max()))
 
 
+def test_backward_plan_matches_call():
+    """BwdPlan (arguments marshalled once) runs the same kernels: bit-identical to
+    attn_bwd, also after a new dO is copied into the planned input (then checked
+    against the oracle)."""
+    say("BwdPlan vs attn_bwd")
+    q, k, v = workloads.make_qkv(2, 50, 50, 16, 16, "fp16", seed=71)
+    do = workloads.make_dout(2, 50, 16, 16, "fp16", seed=72)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    O, L = ea.attn_fwd(qd, kd, vd, softmax_scale=0.25, causal=True)
+    plan = ea.BwdPlan(qd, kd, vd, O, dod, L, 0.25, True)
+    got = [t.clone() for t in plan()]
+    ref = ea.attn_bwd(qd, kd, vd, O, dod, L, softmax_scale=0.25, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(got, ref):
+        assert torch.equal(x, y)
+    do2 = workloads.make_dout(2, 50, 16, 16, "fp16", seed=73)
+    dod.copy_(do2.to(DEV))
+    dq, dk, dv = plan()
+    torch.cuda.synchronize()
+    check_full(dq, dk, dv, oracle.attention_bwd(*host64(q, k, v, do2), 0.25, True), "fp16", "plan after new dO")
+
+
 def test_bwd_deterministic():
     say("bwd determinism")
     q, k, v = workloads.make_qkv(1, 300, 300, 4, 128, "bf16", seed=12, h_kv=2)
