@@ -61,11 +61,12 @@ template <int D> struct Swz {
 // accumulated against the same m, so O/l is the exact softmax (Lab Notes 07,
 // section 3.3: rescaling by the running maximum keeps the result exact).  The
 // common step computes P against the current m without taking a maximum at all;
-// only when a row has no reference yet, or a partial row sum exceeds 2^64 (a
-// score more than 64 above m: P would lose range), does a rare step take the
-// tile's row maxima, move m up to them, multiply O and l by 2^(m_old - m_new)
-// and recompute the tile.  So m never falls below the running maximum by more
-// than 64 and no exponent overflows; rows whose scores fall far below m only
+// only when a row has no reference yet, or a lane's partial row sum exceeds PMAX
+// (2^15 for fp16, whose P must stay below its largest finite value 65504 once
+// rounded; 2^64 for bf16), does a rare step take the tile's row maxima, move m up
+// to them, multiply O and l by 2^(m_old - m_new) and recompute the tile.  So every
+// rounded P stays finite, m never falls below the running maximum by more than
+// log2(PMAX), and no exponent overflows; rows whose scores fall far below m only
 // lose terms that are negligible against the row's maximum.
 template <int N> struct IC { static constexpr int value = N; };
 
@@ -116,7 +117,11 @@ void fwdp_kernel(const FwdParams p) {
   static_assert(NBUF == 2 || NBUF == 4 || NBUF == 8, "the step loop is unrolled by NBUF");
   constexpr int P = NBUF - 1;                   // prefetch distance in tiles
   constexpr int PAIR = 2 * WL;                  // loads of one (K, V) pair per wave
-  constexpr float PMAX = 0x1p64f;               // bound on a partial row sum of P
+  // Bound on a lane's partial row sum of P before a rebase is forced.  Every P of
+  // the lane is at most that sum, and P is rounded to the input type before the
+  // P V product: fp16's largest finite value is 65504, so its bound is 2^15; bf16
+  // has fp32's exponent range, where 2^64 keeps rebases rare.
+  constexpr float PMAX = T_ == kFP16 ? 0x1p15f : 0x1p64f;
 
   __shared__ __attribute__((aligned(1024))) char kbuf[NBUF][TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf[NBUF][TILE];

@@ -551,10 +551,33 @@ def test_sample_rows():
     assert small[0] == list(range(50))
 
 
+# The benchmark's five workloads, written out field by field: (dtype, b, s_q, s_k,
+# h, d, causal, kind, sampled rows per head).  Provenance: issue #1335's timing
+# script parametrises (batch, seq, heads, embed) over (2, 50, 16, 256) and
+# (512, 150, 16, 256) in fp16 with head dim embed / heads = 16; "LLM Lab Notes 07",
+# §2 runs bf16 (4, 512, 32, 128); issue #1248's decode question is batch 1, one
+# query, 16 heads, head dim 128 (here over a 32768-key cache); the fifth is a long
+# causal bf16 prefill checked on 256 seeded rows per head.  Seeds 42 throughout.
+EXPECTED_WORKLOADS = {
+    "C1": ("fp16", 2, 50, 50, 16, 16, False, "prefill", 0),
+    "C2": ("fp16", 512, 150, 150, 16, 16, False, "prefill", 0),
+    "C3": ("bf16", 4, 512, 512, 32, 128, False, "prefill", 0),
+    "C4": ("bf16", 1, 1, 32768, 16, 128, False, "decode", 0),
+    "C5": ("bf16", 1, 16384, 16384, 32, 128, True, "prefill", 256),
+}
+
+
 def test_workload_table():
     W = workloads.WORKLOADS
-    assert [W[c].d for c in ("C1", "C2", "C3", "C4", "C5")] == [16, 16, 128, 128, 128]
-    assert W["C5"].causal and not W["C3"].causal
-    assert W["C4"].s_q == 1 and W["C4"].s_k == 32768 and W["C4"].kind == "decode"
-    assert W["C2"].b == 512 and W["C2"].s_q == 150
-    assert abs(W["C3"].scale - 1 / math.sqrt(128)) < 1e-15
+    assert sorted(W) == sorted(EXPECTED_WORKLOADS)
+    for name, exp in EXPECTED_WORKLOADS.items():
+        w = W[name]
+        got = (w.dtype, w.b, w.s_q, w.s_k, w.h, w.d, w.causal, w.kind, w.sample_rows)
+        assert got == exp, name
+        assert w.name == name
+        assert abs(w.scale - 1 / math.sqrt(w.d)) < 1e-15  # scale = 1/sqrt(d) on every workload
+        assert w.torch_dtype == {"fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    # the drawn tensors have the workload's shapes and dtype (seed 42 by default)
+    q, k, v = workloads.make_qkv(2, 5, 7, 3, 16, "fp16")
+    q2, _, _ = workloads.make_qkv(2, 5, 7, 3, 16, "fp16", seed=42)
+    assert torch.equal(q, q2) and q.shape == (2, 5, 3, 16) and k.shape == v.shape == (2, 7, 3, 16)
