@@ -15,6 +15,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libattn.so")
+# The HBM read probe (include/attn_probe.h) the benchmark measures the read
+# ceiling with; a library of its own, outside the attention boundary.
+PROBE_LIB = os.path.join(HERE, "libattn_probe.so")
+PROBE_SRC = "attn_probe.hip"
 
 # (source, object name, extra flags).  The prefill kernels are compiled once per
 # (input type, causal, paged cache) triple so that the eight sets build in parallel.
@@ -45,11 +49,12 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link ``libattn.so``. Returns its path."""
+    """Compile every source for gfx950 and link ``libattn.so`` (and the read probe
+    ``libattn_probe.so``). Returns the path of ``libattn.so``."""
     cc = hipcc()
     objs = []
     procs = []
-    for src, name, extra in SOURCES:
+    for src, name, extra in [*SOURCES, (PROBE_SRC, "attn_probe", [])]:
         obj = os.path.join(HERE, "_build", name + ".o")
         os.makedirs(os.path.dirname(obj), exist_ok=True)
         cmd = [cc, *HIP_FLAGS, *VGPR_ACC_FLAGS, *extra, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -72,12 +77,14 @@ def build(verbose: bool = False) -> str:
     if failed:
         msg = "\n\n".join(f"--- {s}\n{t}" for s, t in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
-    tmp = LIB + ".tmp"
-    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    probe_obj = objs.pop()
+    for out, parts in ((LIB, objs), (PROBE_LIB, [probe_obj])):
+        tmp = out + ".tmp"
+        cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *parts, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
     return LIB
 
 

@@ -415,6 +415,7 @@ attn_status attn_combine(int32_t num_splits, int64_t b, int64_t h, int64_t s_q, 
   if (st != ATTN_OK) return st;
   if (b * h * s_q > 0x7fffffff) return ATTN_E_SHAPE;
   if (!headdim_ok(d)) return ATTN_E_HEADDIM;
+  if (b * h * s_q * (d / 16) > 0x7fffffff) return ATTN_E_SHAPE;  // one wave per 16 columns of a row
   if (!aligned16(o_part) || !aligned4(lse_part) || !aligned16(o) || !strides_ok(o_stride) ||
       (lse && !aligned4(lse)))
     return ATTN_E_LAYOUT;

@@ -35,6 +35,24 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
+def test_probe_library_exports_every_declared_symbol():
+    from exact_attention_64_amd import _probe
+    text = open(os.path.join(ROOT, "include", "attn_probe.h")).read()
+    names = sorted(set(re.findall(r"^\s*int32_t\s+(attn_\w+)\s*\(", text, re.M)))
+    assert set(names) == set(_probe.EXPORTS), names
+    L = _probe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    # host-side checks, nothing launched
+    assert L.attn_probe_read(None, 1024, 1024, 1024, FAKE, 1, None) == -1
+    assert L.attn_probe_read(FAKE, 1000, 1000, 1000, FAKE, 1, None) == -3   # not a multiple of 16
+    assert L.attn_probe_read(FAKE, 1024, 512, 256, FAKE, 1, None) == -3     # chunk > stride
+    assert L.attn_probe_read(FAKE, 1024, 48, 64, FAKE, 1, None) == -3       # bytes not whole chunks
+    assert L.attn_probe_read(FAKE + 8, 1024, 1024, 1024, FAKE, 1, None) == -5
+    assert L.attn_probe_read(FAKE, 1024, 1024, 1024, FAKE, -2, None) == -3
+    assert L.attn_probe_grid(-1) == -3 and L.attn_probe_grid(37) == 37
+
+
 def test_struct_layout_matches_c(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(r'''

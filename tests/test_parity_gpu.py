@@ -570,3 +570,22 @@ def test_forward_plan_matches_call():
     torch.cuda.synchronize()
     O_ref, L_ref = oracle.attention(*host64(*new), 0.25, True)
     check(O1, L1, O_ref, L_ref, "fp16", "plan after new inputs")
+
+
+def test_read_probe_sums_what_it_reads():
+    # The benchmark's HBM read probe (include/attn_probe.h): the per-work-group
+    # wrapping sums of the 32-bit words it read add up to the host's sum of the
+    # same words, contiguous and strided.
+    from exact_attention_64_amd import _probe
+    say("read probe checksum")
+    g = torch.Generator().manual_seed(1)
+    x = torch.randint(-2 ** 31, 2 ** 31 - 1, (3 * 1024 * 1024 + 4,), generator=g, dtype=torch.int32)
+    u = x.to(torch.int64) & 0xFFFFFFFF
+    xd = x.to(DEV)
+    for nb, ch, st, gr in [(x.numel() * 4 - 16, 0, 0, 0), (1 << 20, 1024, 4096, 7), (4096 * 16, 64, 192, 300)]:
+        sink = _probe.probe_read(xd, nb, ch, st, grid=gr)
+        torch.cuda.synchronize()
+        ch, st = ch or nb, st or ch or nb
+        want = int(torch.cat([u[c * st // 4: c * st // 4 + ch // 4] for c in range(nb // ch)]).sum()) % 2 ** 32
+        got = int((sink.cpu().to(torch.int64) & 0xFFFFFFFF).sum()) % 2 ** 32
+        assert got == want, (nb, ch, st, gr)
