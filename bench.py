@@ -7,13 +7,22 @@ One step = one pass of the whole path over resident synthetic inputs:
     (bf16, b=1, s_q=1, s_k=32768, h=16, d=128), split count from the
     compute-unit heuristic.
 ``value`` is the prefill throughput in TFLOP/s (algorithmic FLOPs: 4*d per
-visible (query, key) pair).  The decode figure (K+V bytes over the time of both
-decode launches, taken between one pair of events, with L2 and the 256 MB MALL
-flushed by a 512 MiB fill before each pass) is reported beside it.  Kernel
+visible (query, key) pair) from the median of the per-launch HIP-event times of
+the timed steps.  The decode figure (K+V bytes over the time of both decode
+launches, taken between one pair of events, with L2 and the 256 MB MALL flushed
+by a 512 MiB fill before each pass; median) is reported beside it.  Kernel
 durations come from HIP events recorded on the stream the kernels run on.
 
-The backward pass (attn_bwd) is reported beside them under "backward": the
-long causal workload and issue #1335's two fp16 head-dim-16 workloads.
+Beside the rooflines the line carries what the device really sustains
+(libattn_probe.so, include/attn_probe.h): the shader clock sampled during
+back-to-back prefill launches, an MFMA loop on random bf16 operands (the
+power-limited matrix-core ceiling) and a plain read of the decode's 268 MB
+(the read ceiling flash-attention issue #1248 compares decoding with).
+
+The backward pass (attn_bwd) is reported under "backward": the long causal
+workload and issue #1335's two fp16 head-dim-16 workloads.  The float64 CPU
+oracle is timed on the four smaller workloads in full and on a row sample of
+the long one ("cpu_baseline").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|decode|backward]
 Prints one JSON line.
@@ -117,9 +126,11 @@ def device_facts(torch, dev):
             "copy_gbs": round(2 * n / (best * 1e-3) / 1e9, 1)}
 
 
-def cpu_baseline(w, budget_s: float = 20.0):
-    """Time the float64 oracle on a bounded sample of the prefill workload: whole
-    heads' worth of seeded query rows until about ``budget_s`` seconds of work."""
+def cpu_baseline(w, budget_s: float = 12.0):
+    """Time the float64 oracle on the machine's host cores: on a bounded sample of the
+    prefill workload (whole heads' worth of seeded query rows until about
+    ``budget_s`` seconds of work), and on the four smaller workloads in full
+    (inputs generated and upcast outside the timed region)."""
     import numpy as np
     import oracle
     import workloads
@@ -131,7 +142,6 @@ def cpu_baseline(w, budget_s: float = 20.0):
     done_flops = 0
     done_rows = 0
     heads = 0
-    t0 = time.perf_counter()
     elapsed = 0.0
     off = w.s_k - w.s_q
     for hi in range(w.h):
@@ -145,6 +155,20 @@ def cpu_baseline(w, budget_s: float = 20.0):
         heads += 1
         if elapsed >= budget_s:
             break
+    del q, k, v
+    per_config = {}
+    for name in ("C1", "C2", "C3", "C4"):
+        wc = workloads.WORKLOADS[name]
+        h64 = [t.to(torch.float64).numpy() for t in workloads.make_workload(wc)]
+        t1 = time.perf_counter()
+        oracle.attention(*h64, wc.scale, wc.causal)
+        dt = time.perf_counter() - t1
+        per_config[name] = dict(workload=wc.note, seconds=round(dt, 3), gflops=round(flops(wc) / dt / 1e9, 2),
+                                full=True)
+        del h64
+    per_config["C5"] = dict(workload=w.note, seconds=round(elapsed, 3),
+                            gflops=round(done_flops / elapsed / 1e9, 2), full=False,
+                            extrapolated_full_s=round(elapsed * flops(w) / done_flops, 1))
     return {
         "value": round(done_flops / elapsed / 1e12, 6),
         "unit": "TFLOP/s",
@@ -153,10 +177,97 @@ def cpu_baseline(w, budget_s: float = 20.0):
         "sample": (f"float64 NumPy oracle, {done_rows} seeded query rows ({len(rows_all[0])} per head, "
                    f"{heads} of {w.h} heads) of the causal s=16384 workload, each over its full key "
                    f"prefix; {done_flops / 1e9:.1f} GFLOP in {elapsed:.2f} s on {cpu_model()}, "
-                   f"{len(os.sched_getaffinity(0))} cores in the affinity mask"),
+                   f"{len(os.sched_getaffinity(0))} cores in the affinity mask; per_config holds the "
+                   f"four smaller workloads timed in full"),
         "seconds": round(elapsed, 3),
         "extrapolated_full_s": round(elapsed * flops(w) / done_flops, 1),
+        "per_config": per_config,
     }
+
+
+def stats_ms(ts):
+    """(median, min, mean) of a list of event times in ms."""
+    ts = sorted(ts)
+    return ts[len(ts) // 2], ts[0], sum(ts) / len(ts)
+
+
+def shader_clock_mhz(torch, probe, run, launches, dev):
+    """The shader clock while ``run`` (one prefill launch) repeats back to back.
+
+    A one-wave probe on a second stream (default priority) reads the cycle counter
+    (shader cycles) and the steady counter at its start and after most of the run.
+    The steady counter's rate is taken from HIP events around the probe running
+    alone for ~20 ms, which also gives the clock of a nearly idle device.
+    Returns (MHz during the run, MHz of the lone probe, peak MHz)."""
+    wall_attr_hz, peak_hz = probe.rates()
+    out = torch.zeros(4, dtype=torch.int64, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    probe.probe_clock(int(wall_attr_hz * 20e-3), dev, None, out)
+    b.record()
+    torch.cuda.synchronize()
+    c0, c1, w0, w1 = out.tolist()
+    secs = a.elapsed_time(b) * 1e-3
+    wall_hz = (w1 - w0) / secs
+    idle_mhz = (c1 - c0) / ((w1 - w0) / wall_hz) / 1e6
+    run()
+    torch.cuda.synchronize()
+    a.record()
+    run()
+    b.record()
+    torch.cuda.synchronize()
+    one_s = a.elapsed_time(b) * 1e-3
+    side = torch.cuda.Stream(dev)
+    with torch.cuda.stream(side):
+        probe.probe_clock(int(wall_hz * one_s * (launches - 2)), dev, side, out)
+    for _ in range(launches):
+        run()
+    torch.cuda.synchronize()
+    c0, c1, w0, w1 = out.tolist()
+    mhz = (c1 - c0) / ((w1 - w0) / wall_hz) / 1e6
+    return round(mhz, 1), round(idle_mhz, 1), round(peak_hz / 1e6, 1)
+
+
+def mfma_ceiling(torch, probe, dev, E):
+    """TFLOP/s of the register-only MFMA loop (8 waves per compute unit, random
+    and constant bf16 operands), median of three calls each."""
+    res = {}
+    for key, rnd in (("random_operands", True), ("constant_operands", False)):
+        ts = []
+        for _ in range(3):
+            a, b = E(), E()
+            a.record()
+            _, _, fl = probe.probe_mfma(2000, rnd, dev)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        med = sorted(ts)[1]
+        res[key] = round(fl / (med * 1e-3) / 1e12, 1)
+    return res
+
+
+def read_ceiling(torch, probe, nbytes, flush, dev, E):
+    """GB/s of a plain 16-byte nontemporal read of ``nbytes`` after a cache flush:
+    the best of a few grid sizes, median of 10 reads each."""
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    best = None
+    for grid in (256, 512, 1024, 2048):
+        sink = torch.empty(grid, dtype=torch.int32, device=dev)
+        ts = []
+        for _ in range(10):
+            flush.fill_(0.0)
+            a, b = E(), E()
+            a.record()
+            probe.probe_read(buf, nbytes, grid=grid, sink=sink)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        med = stats_ms(ts)[0]
+        if best is None or med < best[0]:
+            best = (med, grid)
+    del buf
+    return {"bytes": nbytes, "us": round(best[0] * 1e3, 2), "gbs": round(nbytes / (best[0] * 1e-3) / 1e9, 1),
+            "grid": best[1]}
 
 
 def bench_backward(torch, ea, workloads, dev, E):
@@ -235,6 +346,7 @@ def main():
 
     import torch
     import exact_attention_64_amd as ea
+    from exact_attention_64_amd import _probe as probe
     import workloads
 
     dev = torch.device("cuda:0")
@@ -304,13 +416,13 @@ def main():
 
     res = {}
     if do_p:
-        p_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-        p_tf = flops(wp) / (p_ms * 1e-3) / 1e12
-        res["prefill"] = dict(ms=p_ms, tflops=p_tf)
+        p_med, p_min, p_mean = stats_ms([e[0].elapsed_time(e[1]) for e in events])
+        res["prefill"] = dict(ms=p_med, ms_min=p_min, ms_mean=p_mean, tflops=flops(wp) / (p_med * 1e-3) / 1e12)
     if do_d:
-        d_ms = sum(e[2].elapsed_time(e[4]) for e in events) / args.steps
-        # Per-kernel durations of the two decode launches (for the roofline),
-        # from their own event pairs in a separate loop after the timed steps.
+        d_med, d_min, d_mean = stats_ms([e[2].elapsed_time(e[4]) for e in events])
+        # Per-kernel durations of the two decode launches, from their own event
+        # pairs in a separate loop after the timed steps (context only: the
+        # decode figure is both launches between one pair of events).
         kev = [[E() for _ in range(4)] for _ in range(args.steps)]
         for e in kev:
             flush.fill_(0.0)
@@ -321,11 +433,38 @@ def main():
             ea.attn_combine(opart, lpart, qd.dtype, out=Od, lse=Ld)
             e[3].record()
         torch.cuda.synchronize()
-        s_ms = sum(e[0].elapsed_time(e[1]) for e in kev) / args.steps
-        c_ms = sum(e[2].elapsed_time(e[3]) for e in kev) / args.steps
+        s_ms = stats_ms([e[0].elapsed_time(e[1]) for e in kev])[0]
+        c_ms = stats_ms([e[2].elapsed_time(e[3]) for e in kev])[0]
         kvb = 2 * 2 * wd.b * wd.s_k * wd.h * wd.d
-        res["decode"] = dict(ms=d_ms, splitkv_ms=s_ms, combine_ms=c_ms, gbs=kvb / (d_ms * 1e-3) / 1e9,
-                             splitkv_gbs=kvb / (s_ms * 1e-3) / 1e9, kv_bytes=kvb, splits=n_splits)
+        # Split-count sweep (issue #1248 compares hard-coded 2/4/8 splits with the
+        # heuristic): split-KV + combine between one event pair, caches flushed,
+        # median of 10 passes per count.
+        sweep = {}
+        for n in sorted({8, 16, 32, 48, 64, 96, 128, n_splits}):
+            op_n = torch.empty((n, wd.b, wd.h, wd.s_q, wd.d), dtype=torch.float32, device=dev)
+            lp_n = torch.empty((n, wd.b, wd.h, wd.s_q), dtype=torch.float32, device=dev)
+            ts = []
+            for _ in range(10):
+                flush.fill_(0.0)
+                a, b = E(), E()
+                a.record()
+                ea.attn_fwd_splitkv(qd, kd, vd, n, wd.scale, False, o_part=op_n, lse_part=lp_n)
+                ea.attn_combine(op_n, lp_n, qd.dtype, out=Od, lse=Ld)
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            sweep[str(n)] = round(stats_ms(ts)[0] * 1e3, 2)
+            del op_n, lp_n
+        res["decode"] = dict(ms=d_med, ms_min=d_min, ms_mean=d_mean, splitkv_ms=s_ms, combine_ms=c_ms,
+                             gbs=kvb / (d_med * 1e-3) / 1e9, kv_bytes=kvb, splits=n_splits, sweep=sweep,
+                             read=read_ceiling(torch, probe, kvb, flush, dev, E))
+
+    # ---- what the device sustains: shader clock during back-to-back prefill
+    # launches, and the power-limited MFMA ceiling of a register-only loop
+    if do_p:
+        run_p = lambda: ea.attn_fwd(qp, kp, vp, wp.scale, wp.causal, out=Op, lse=Lp)  # noqa: E731
+        res["prefill"]["sclk"] = shader_clock_mhz(torch, probe, run_p, 12, dev)
+        res["prefill"]["mfma_ceiling"] = mfma_ceiling(torch, probe, dev, E)
 
     # ---- side table: the three smaller prefill workloads.  Event time per launch
     # (median, min, mean over 200 launches for C1/C2, 20 for C3, caches flushed
@@ -405,7 +544,7 @@ def main():
         # heads, a 4096-key cache, 1 or 4 new tokens): split-KV + combine with the
         # heuristic's split count, over the contiguous cache and over a paged one
         # (64-key blocks, scattered), one event pair around both launches after a
-        # cache flush, mean of 20 passes.
+        # cache flush, median of 20 passes.
         for s_q in (1, 4):
             q, k, v = (t.to(dev) for t in workloads.make_qkv(8, s_q, 4096, 48, 128, "bf16", seed=19, h_kv=8))
             _, kc, vc, table, sl = (t.to(dev) for t in workloads.make_paged(8, s_q, 48, 128, "bf16", [4096] * 8,
@@ -433,12 +572,13 @@ def main():
                     b.record()
                     torch.cuda.synchronize()
                     ts.append(a.elapsed_time(b))
-                mean = sum(ts) / len(ts)
+                med, mn, mean = stats_ms(ts)
                 side[f"gqa_decode_{kind}_s_q{s_q}"] = dict(
                     workload=f"bf16 causal b=8 s_q={s_q} s_k=4096 h=48 h_kv=8 d=128, {kind} K/V"
                              + (" (64-key blocks)" if kind == "paged" else "") + ", split-KV + combine",
-                    us=round(mean * 1e3, 2), splits=n, kv_gbs=round(kvb / (mean * 1e-3) / 1e9, 1),
-                    frac_hbm=round(kvb / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+                    us=round(med * 1e3, 2), us_min=round(mn * 1e3, 2), us_mean=round(mean * 1e3, 2), splits=n,
+                    kv_gbs=round(kvb / (med * 1e-3) / 1e9, 1),
+                    frac_hbm=round(kvb / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
             del q, k, v, kc, vc, table, sl, op, lp, O
         del flush_s
 
@@ -463,35 +603,50 @@ def main():
                            "(attn_fwd_splitkv + attn_combine)" if do_d else ""),
             "b": wp.b, "s_q": wp.s_q, "s_k": wp.s_k, "h": wp.h, "d": wp.d, "causal": True,
         }
+        sclk, idle_mhz, peak_mhz = p["sclk"]
+        ceil = p["mfma_ceiling"]
         out["roofline"] = {
             "bound": "mfma", "achieved": round(p["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4),
             "traffic": read_traffic("prefill"),
-            "kernel": "fwdp_kernel (attn_fwd, d >= 64 prefill)", "avg_launch_ms": round(p["ms"], 4),
+            "kernel": "fwdp_kernel (attn_fwd, d >= 64 prefill)",
+            "launch_ms_median": round(p["ms"], 4), "launch_ms_min": round(p["ms_min"], 4),
+            "launch_ms_mean": round(p["ms_mean"], 4), "launches": args.steps,
             "flops_per_launch": flops(wp),
+            "sclk_mhz": sclk, "sclk_idle_probe_mhz": idle_mhz, "sclk_peak_mhz": peak_mhz,
+            "frac_at_sclk": round(p["tflops"] / (PEAK_BF16_TFLOPS * sclk / peak_mhz), 4) if sclk else None,
+            "mfma_loop_random_tflops": ceil["random_operands"],
+            "mfma_loop_constant_tflops": ceil["constant_operands"],
+            "frac_of_random_mfma_loop": round(p["tflops"] / ceil["random_operands"], 4),
         }
     if do_d:
         dd = res["decode"]
+        rd = dd["read"]
         dec = {
             "value": round(dd["gbs"], 1), "unit": "GB/s", "us": round(dd["ms"] * 1e3, 2),
+            "us_min": round(dd["ms_min"] * 1e3, 2), "us_mean": round(dd["ms_mean"] * 1e3, 2),
             "splitkv_us": round(dd["splitkv_ms"] * 1e3, 2), "combine_us": round(dd["combine_ms"] * 1e3, 2),
             "splits": dd["splits"], "frac_hbm": round(dd["gbs"] / PEAK_HBM_GBS, 4),
+            "read_ceiling": rd, "frac_of_read_ceiling": round(dd["gbs"] / rd["gbs"], 4),
+            "split_sweep_us": dd["sweep"],
         }
-        rd = {
-            "bound": "hbm", "achieved": round(dd["splitkv_gbs"], 1), "peak": PEAK_HBM_GBS,
-            "unit": "GB/s", "frac": round(dd["splitkv_gbs"] / PEAK_HBM_GBS, 4),
-            "traffic": read_traffic("decode"), "kernel": "decode_kernel (attn_fwd_splitkv, s_q = 1)",
-            "avg_launch_ms": round(dd["splitkv_ms"], 4), "bytes_per_launch": dd["kv_bytes"],
+        rdl = {
+            "bound": "hbm", "achieved": round(dd["gbs"], 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(dd["gbs"] / PEAK_HBM_GBS, 4),
+            "traffic": read_traffic("decode"),
+            "kernel": "decode_kernel + combine_kernel (attn_fwd_splitkv + attn_combine, s_q = 1)",
+            "launch_us_median": round(dd["ms"] * 1e3, 2), "bytes_per_launch": dd["kv_bytes"],
+            "splitkv_only_gbs": round(dd["kv_bytes"] / (dd["splitkv_ms"] * 1e-3) / 1e9, 1),
         }
         if do_p:
             out["decode"] = dec
-            out["roofline_decode"] = rd
+            out["roofline_decode"] = rdl
         else:
             out.update(value=dec["value"], unit="GB/s")
             out["config"] = {"workload": "split-KV decode bf16 b=1 s_q=1 s_k=32768 h=16 d=128",
                              "b": wd.b, "s_q": wd.s_q, "s_k": wd.s_k, "h": wd.h, "d": wd.d}
             out["decode"] = dec
-            out["roofline"] = rd
+            out["roofline"] = rdl
     if side:
         out["other_workloads"] = side
     if args.only in ("all", "backward") and not args.no_small:

@@ -10,7 +10,7 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 PROBE_PATH = os.path.join(HERE, "libattn_probe.so")
-EXPORTS = ("attn_probe_read", "attn_probe_grid")
+EXPORTS = ("attn_probe_read", "attn_probe_mfma", "attn_probe_clock", "attn_probe_rates", "attn_probe_grid")
 
 _lib = None
 _lock = threading.Lock()
@@ -30,6 +30,13 @@ def lib():
             L.attn_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
             L.attn_probe_read.restype = ctypes.c_int32
+            L.attn_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+            L.attn_probe_mfma.restype = ctypes.c_int32
+            L.attn_probe_clock.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+            L.attn_probe_clock.restype = ctypes.c_int32
+            L.attn_probe_rates.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+            L.attn_probe_rates.restype = ctypes.c_int32
             L.attn_probe_grid.argtypes = [ctypes.c_int32]
             L.attn_probe_grid.restype = ctypes.c_int32
             _lib = L
@@ -61,3 +68,41 @@ def probe_read(buf: torch.Tensor, nbytes: int = 0, chunk: int = 0, stride: int =
     if rc != 0:
         raise RuntimeError(f"attn_probe_read: status {rc}")
     return sink
+
+
+def _stream(dev, stream):
+    return stream.cuda_stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+
+
+def probe_mfma(iters: int, random_operands: bool, device="cuda:0", stream=None):
+    """Enqueue the register-only MFMA loop; returns (out, ticks, flops): ``ticks``
+    (int64 (2,)) receives the cycle- and steady-counter deltas of wave 0."""
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    out = torch.empty(cus * 512, dtype=torch.float32, device=device)
+    ticks = torch.zeros(2, dtype=torch.int64, device=device)
+    rc = lib().attn_probe_mfma(ctypes.c_void_p(out.data_ptr()), iters, int(bool(random_operands)),
+                               ctypes.c_void_p(ticks.data_ptr()), ctypes.c_void_p(_stream(device, stream)))
+    if rc != 0:
+        raise RuntimeError(f"attn_probe_mfma: status {rc}")
+    return out, ticks, iters * 16 * 32768 * 8 * cus
+
+
+def probe_clock(wall_ticks: int, device="cuda:0", stream=None, out=None):
+    """Enqueue the one-wave clock probe; ``out`` (int64 (4,)) receives the cycle
+    counter and the steady counter at its start and its end."""
+    if out is None:
+        out = torch.zeros(4, dtype=torch.int64, device=device)
+    rc = lib().attn_probe_clock(ctypes.c_void_p(out.data_ptr()), int(wall_ticks),
+                                ctypes.c_void_p(_stream(device, stream)))
+    if rc != 0:
+        raise RuntimeError(f"attn_probe_clock: status {rc}")
+    return out
+
+
+def rates():
+    """(steady-counter rate, peak shader clock) of the current device, in Hz."""
+    w, c = ctypes.c_int64(), ctypes.c_int64()
+    rc = lib().attn_probe_rates(ctypes.byref(w), ctypes.byref(c))
+    if rc != 0:
+        raise RuntimeError(f"attn_probe_rates: status {rc}")
+    return w.value * 1000, c.value * 1000

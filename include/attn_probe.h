@@ -36,6 +36,36 @@ extern "C" {
 int32_t attn_probe_read(const void *buf, int64_t bytes, int64_t chunk, int64_t stride,
                         uint32_t *sink, int32_t grid, void *stream);
 
+/* MFMA throughput probe: every compute unit runs one work-group of 8 waves (two
+ * per SIMD, as the prefill kernel does) that issues `iters` x 16
+ * v_mfma_f32_32x32x16_bf16 in four accumulator chains on registers only.  With
+ * random_operands != 0 the A and B operands are random bf16 values (random
+ * sign, exponent and mantissa bits, magnitudes in [1/8, 2)) that change
+ * from one instruction to the next (the switching of real attention data; the
+ * device's power limit then lowers its clock); with 0 they are constant.  Writes
+ * one float per thread to `out` (8 * 64 * compute units floats) so nothing is
+ * optimised away, and to `ticks` (two uint64) the cycle-counter and steady-counter
+ * deltas of wave 0 over its loop (which it may finish early: of two waves on a
+ * SIMD the older one tends to be served first).  Flops per call: iters * 16 * 32768 * 8 *
+ * compute units.  Returns 0, -1 (NULL), -3 (iters < 1), -8 (no device) or -9. */
+int32_t attn_probe_mfma(float *out, int32_t iters, int32_t random_operands, uint64_t *ticks,
+                        void *stream);
+
+/* Clock probe: one wave that reads the cycle counter (clock64(): shader
+ * cycles) and the steady counter (wall_clock64(), at a constant rate that
+ * hipDeviceAttributeWallClockRate reports) when it starts and again once the steady
+ * counter has advanced by `wall_ticks` (at most 2^31 of them; the wave sleeps
+ * between reads), and writes the four values to `out` (four uint64).  Launched on
+ * a second stream beside a long kernel it samples the shader clock while that
+ * kernel runs (one wave of few registers fits next to it on a compute unit).
+ * Returns 0, -1 (NULL), -3 (wall_ticks outside [1, 2^31]) or -9. */
+int32_t attn_probe_clock(uint64_t *out, int64_t wall_ticks, void *stream);
+
+/* The current device's steady-counter rate and peak shader clock, in kHz
+ * (hipDeviceAttributeWallClockRate and hipDeviceAttributeClockRate).  Returns 0,
+ * -1 (NULL) or -8 (no device). */
+int32_t attn_probe_rates(int64_t *wall_khz, int64_t *peak_sclk_khz);
+
 /* Work-groups attn_probe_read launches for `grid` (the count `sink` must hold):
  * grid itself when > 0, else four per compute unit of the current device
  * (negative on error, as above). */

@@ -51,6 +51,12 @@ def test_probe_library_exports_every_declared_symbol():
     assert L.attn_probe_read(FAKE + 8, 1024, 1024, 1024, FAKE, 1, None) == -5
     assert L.attn_probe_read(FAKE, 1024, 1024, 1024, FAKE, -2, None) == -3
     assert L.attn_probe_grid(-1) == -3 and L.attn_probe_grid(37) == 37
+    assert L.attn_probe_mfma(None, 10, 1, FAKE, None) == -1
+    assert L.attn_probe_mfma(FAKE, 0, 1, FAKE, None) == -3
+    assert L.attn_probe_clock(None, 100, None) == -1
+    assert L.attn_probe_clock(FAKE, 0, None) == -3
+    assert L.attn_probe_clock(FAKE, (1 << 31) + 1, None) == -3
+    assert L.attn_probe_rates(None, None) == -1
 
 
 def test_struct_layout_matches_c(tmp_path):

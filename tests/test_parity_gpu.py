@@ -589,3 +589,38 @@ def test_read_probe_sums_what_it_reads():
         want = int(torch.cat([u[c * st // 4: c * st // 4 + ch // 4] for c in range(nb // ch)]).sum()) % 2 ** 32
         got = int((sink.cpu().to(torch.int64) & 0xFFFFFFFF).sum()) % 2 ** 32
         assert got == want, (nb, ch, st, gr)
+
+
+def test_mfma_and_clock_probes_run():
+    # The benchmark's MFMA-loop and clock probes: counters advance, the shader
+    # clock they give lies between 100 MHz and the device's peak (plus 5%), and the
+    # constant-operand loop's accumulators hold the exact count of products
+    # (every operand is 1.0: each step adds 16 per element per MFMA chain).
+    from exact_attention_64_amd import _probe
+    say("mfma / clock probes")
+    out, ticks, fl = _probe.probe_mfma(50, False)
+    torch.cuda.synchronize()
+    assert ticks[0].item() > 0 and ticks[1].item() > 0
+    # four chains of 4 MFMAs per step, 16 products of 1.0 each per element: the
+    # final sum over 4 chains x 16 elements is 50 * 4 * 16 * 16 * 4
+    assert torch.all(out == 50 * 4 * 16 * 16 * 4)
+    # 16 MFMAs of 32 cycles per loop iteration; wave 0 shares its SIMD with one
+    # other wave, and runs 512 (served first) to 1024 cycles per iteration
+    assert 500 < ticks[0].item() / 50 < 1100
+    wall_attr_hz, peak_hz = _probe.rates()
+    assert wall_attr_hz > 0 and peak_hz > 0
+    # the steady counter's rate, from HIP events around a probe that runs ~20 ms;
+    # the cycle counter counts shader cycles
+    n = int(wall_attr_hz * 20e-3)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    c = _probe.probe_clock(n)
+    b.record()
+    torch.cuda.synchronize()
+    c0, c1, w0, w1 = c.tolist()
+    assert w1 - w0 >= n and c1 > c0
+    secs = a.elapsed_time(b) * 1e-3
+    wall_hz = (w1 - w0) / secs
+    assert 0.75 * wall_attr_hz < wall_hz < 1.25 * wall_attr_hz, (wall_hz, wall_attr_hz)
+    mhz = (c1 - c0) / ((w1 - w0) / wall_hz) / 1e6
+    assert 100 < mhz < peak_hz / 1e6 * 1.05, mhz
