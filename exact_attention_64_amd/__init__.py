@@ -5,13 +5,13 @@ split-KV and LSE combine, over contiguous or paged K/V, as hand-written HIP kern
 The HIP library is loaded on first use; functions raise if it is not built.
 """
 from ._lib import (ATTN_BF16, ATTN_FP16, ATTN_MAX_SPLITS, EXPORTS, AttnArgs, AttnError,
-                   AttnPagedArgs, AttnBwdArgs, BwdPlan, FwdPlan, attn_bwd, attn_combine, attn_decode, attn_decode_paged, attn_fwd,
+                   AttnPagedArgs, AttnBwdArgs, BwdPlan, FwdPlan, attn_bwd, attn_bwd_noalloc, attn_combine, attn_decode, attn_decode_paged, attn_fwd,
                    attn_fwd_paged, attn_fwd_splitkv, attn_fwd_splitkv_paged, attn_num_splits,
                    attn_num_splits_for, attn_num_splits_paged, lib, make_args, make_paged_args, make_bwd_args,
                    status_str)
 
 __all__ = ["ATTN_BF16", "ATTN_FP16", "ATTN_MAX_SPLITS", "EXPORTS", "AttnArgs", "AttnError",
-           "AttnPagedArgs", "AttnBwdArgs", "BwdPlan", "FwdPlan", "attn_bwd", "attn_combine", "attn_decode", "attn_decode_paged", "attn_fwd",
+           "AttnPagedArgs", "AttnBwdArgs", "BwdPlan", "FwdPlan", "attn_bwd", "attn_bwd_noalloc", "attn_combine", "attn_decode", "attn_decode_paged", "attn_fwd",
            "attn_fwd_paged", "attn_fwd_splitkv", "attn_fwd_splitkv_paged", "attn_num_splits",
            "attn_num_splits_for", "attn_num_splits_paged", "lib", "make_args", "make_paged_args", "make_bwd_args",
            "status_str"]

@@ -25,14 +25,14 @@ _CODE_DTYPE = {v: k for k, v in _DTYPE_CODE.items()}
 
 STATUS = {0: "ATTN_OK", -1: "ATTN_E_NULL", -2: "ATTN_E_DTYPE", -3: "ATTN_E_SHAPE",
           -4: "ATTN_E_HEADDIM", -5: "ATTN_E_LAYOUT", -6: "ATTN_E_SCALE", -7: "ATTN_E_SPLITS",
-          -8: "ATTN_E_DEVICE", -9: "ATTN_E_LAUNCH"}
+          -8: "ATTN_E_DEVICE", -9: "ATTN_E_LAUNCH", -10: "ATTN_E_SCRATCH"}
 
 I64x3 = ctypes.c_int64 * 3
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_num_splits", "attn_num_splits_for", "attn_num_splits_kv",
            "attn_num_splits_kv_for", "attn_fwd_splitkv", "attn_combine", "attn_fwd_paged",
-           "attn_fwd_splitkv_paged", "attn_num_splits_paged", "attn_bwd", "attn_status_str")
+           "attn_fwd_splitkv_paged", "attn_num_splits_paged", "attn_bwd", "attn_bwd_noalloc", "attn_status_str")
 
 
 class AttnArgs(ctypes.Structure):
@@ -136,6 +136,8 @@ def lib():
             L.attn_num_splits_paged.restype = ctypes.c_int32
             L.attn_bwd.argtypes = [P(AttnBwdArgs), ctypes.c_void_p]
             L.attn_bwd.restype = ctypes.c_int32
+            L.attn_bwd_noalloc.argtypes = [P(AttnBwdArgs), ctypes.c_void_p]
+            L.attn_bwd_noalloc.restype = ctypes.c_int32
             L.attn_status_str.argtypes = [ctypes.c_int32]
             L.attn_status_str.restype = ctypes.c_char_p
             _lib = L
@@ -414,6 +416,8 @@ def make_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, delta, softmax_scale=None
         if tuple(t.shape) != tuple(shp):
             raise ValueError(f"{name} must have shape {tuple(shp)}, got {tuple(t.shape)}")
     for name, t in (("lse", lse), ("delta", delta)):
+        if t is None and name == "delta":
+            continue
         if tuple(t.shape) != (b, h, s_q) or t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous float32 (b, h, s_q) tensor")
     if softmax_scale is None:
@@ -428,7 +432,7 @@ def make_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, delta, softmax_scale=None
     a.lse = lse.data_ptr()
     a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
     a.dq_stride, a.dk_stride, a.dv_stride = _bshd("dq", dq), _bshd("dk", dk), _bshd("dv", dv)
-    a.delta = delta.data_ptr()
+    a.delta = delta.data_ptr() if delta is not None else None
     a.softmax_scale = float(softmax_scale)
     return a
 
@@ -451,6 +455,14 @@ def attn_bwd(q, k, v, out, dout, lse, softmax_scale=None, causal=False, dq=None,
         delta = torch.empty((b, h, s_q), dtype=torch.float32, device=q.device)
     a = make_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, delta, softmax_scale, causal)
     _check(lib().attn_bwd(ctypes.byref(a), _stream_ptr(q, stream)))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, out, dout, lse, dq, dk, dv, softmax_scale=None, causal=False, stream=None):
+    """``attn_bwd`` with delta in the library's static device buffer: nothing is
+    allocated, so dq, dk and dv must be given (written in place, returned)."""
+    a = make_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, None, softmax_scale, causal)
+    _check(lib().attn_bwd_noalloc(ctypes.byref(a), _stream_ptr(q, stream)))
     return dq, dk, dv
 
 

@@ -10,6 +10,8 @@
 #include "../../include/attn.h"
 #include "attn_internal.h"
 
+static_assert(attn::kBwdScratchFloats == ATTN_BWD_SCRATCH_ROWS, "the scratch size is part of the ABI");
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -215,6 +217,7 @@ const char* attn_status_str(int32_t s) {
     case ATTN_E_SPLITS: return "num_splits must be in [1, min(s_k, ATTN_MAX_SPLITS)]";
     case ATTN_E_DEVICE: return "no usable gfx950 device";
     case ATTN_E_LAUNCH: return "kernel launch failed";
+    case ATTN_E_SCRATCH: return "the problem needs more than the library's static scratch (b*h*s_q > ATTN_BWD_SCRATCH_ROWS)";
     default: return "unknown status";
   }
 }
@@ -343,10 +346,16 @@ attn_status attn_num_splits_paged(int64_t b, int64_t h, int64_t h_kv, int64_t s_
   return ATTN_OK;
 }
 
-attn_status attn_bwd(const attn_bwd_args* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and launch shared by attn_bwd (delta from the caller) and
+// attn_bwd_noalloc (delta in the library's static scratch): `delta` is the
+// buffer the kernels use; nullptr means the static one.
+attn_status bwd_run(const attn_bwd_args* a, float* delta, void* stream) {
   if (!a) return ATTN_E_NULL;
-  if (!a->q || !a->k || !a->v || !a->o || !a->dout || !a->lse || !a->dq || !a->dk || !a->dv || !a->delta)
-    return ATTN_E_NULL;
+  if (!a->q || !a->k || !a->v || !a->o || !a->dout || !a->lse || !a->dq || !a->dk || !a->dv) return ATTN_E_NULL;
   if (a->dtype != ATTN_FP16 && a->dtype != ATTN_BF16) return ATTN_E_DTYPE;
   attn_status st = check_shape(a->b, a->h, a->s_q, a->s_k);
   if (st != ATTN_OK) return st;
@@ -362,14 +371,19 @@ attn_status attn_bwd(const attn_bwd_args* a, void* stream) {
   const void* t16[] = {a->q, a->k, a->v, a->o, a->dout, a->dq, a->dk, a->dv};
   for (const void* t : t16)
     if (!aligned16(t)) return ATTN_E_LAYOUT;
-  if (!aligned4(a->lse) || !aligned4(a->delta)) return ATTN_E_LAYOUT;
+  if (!aligned4(a->lse) || (delta && !aligned4(delta))) return ATTN_E_LAYOUT;
   const int64_t* strides[] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride,
                               a->dout_stride, a->dq_stride, a->dk_stride, a->dv_stride};
   for (const int64_t* s : strides)
     if (!strides_ok(s)) return ATTN_E_LAYOUT;
   if (!std::isfinite(a->softmax_scale)) return ATTN_E_SCALE;
+  if (!delta && a->b * a->h * a->s_q > attn::kBwdScratchFloats) return ATTN_E_SCRATCH;
   st = current_device_ok();
   if (st != ATTN_OK) return st;
+  if (!delta && attn::bwd_scratch(&delta) != hipSuccess) {
+    (void)hipGetLastError();
+    return ATTN_E_DEVICE;
+  }
   attn::BwdParams p;
   std::memset(&p, 0, sizeof(p));
   p.q = a->q;
@@ -378,7 +392,7 @@ attn_status attn_bwd(const attn_bwd_args* a, void* stream) {
   p.o = a->o;
   p.dout = a->dout;
   p.lse = a->lse;
-  p.delta = a->delta;
+  p.delta = delta;
   p.dq = a->dq;
   p.dk = a->dk;
   p.dv = a->dv;
@@ -405,6 +419,17 @@ attn_status attn_bwd(const attn_bwd_args* a, void* stream) {
   hipError_t e = attn::launch_bwd(p, a->dtype, a->causal != 0, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_bwd(const attn_bwd_args* a, void* stream) {
+  if (a && !a->delta) return ATTN_E_NULL;
+  return bwd_run(a, a ? a->delta : nullptr, stream);
+}
+
+attn_status attn_bwd_noalloc(const attn_bwd_args* a, void* stream) { return bwd_run(a, nullptr, stream); }
 
 attn_status attn_combine(int32_t num_splits, int64_t b, int64_t h, int64_t s_q, int64_t d,
                          const float* o_part, const float* lse_part, int32_t dtype, void* o,

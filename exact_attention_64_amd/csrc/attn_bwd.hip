@@ -32,6 +32,8 @@
 //                      order.
 // Every product runs on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulation;
 // P and dS are rounded to the input type before they feed a product.
+#include <mutex>
+
 #include "attn_common.h"
 
 #ifndef ATTN_BWD_SMALL_NW
@@ -646,6 +648,31 @@ static hipError_t launch_bwd_c(const BwdParams& p, hipStream_t st) {
     case 64: return launch_bwd_t<T_, 64, CAUSAL>(p, st);
     default: return launch_bwd_t<T_, 128, CAUSAL>(p, st);
   }
+}
+
+// Static delta buffer of attn_bwd_noalloc (for callers that cannot allocate):
+// one copy per device, held until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only that
+// address is handed to the kernels.
+static __device__ __align__(256) float scratch[kBwdScratchFloats];
+
+hipError_t bwd_scratch(float** out) {
+  static std::mutex mu;
+  static float* addr[64] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(ptr);
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_bwd(const BwdParams& p, int dtype, bool causal, hipStream_t st) {

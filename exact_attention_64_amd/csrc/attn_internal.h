@@ -148,5 +148,9 @@ inline hipError_t launch_fwd(const FwdParams& p, int dtype, bool causal, bool sp
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t st);
 // Backward: dQ (which also writes delta), then dK/dV, enqueued in that order on `st`.
 hipError_t launch_bwd(const BwdParams& p, int dtype, bool causal, hipStream_t st);
+// Device address of the backward's static delta scratch (kBwdScratchFloats fp32)
+// on the current device, resolved once per device (attn_bwd.hip).
+constexpr int64_t kBwdScratchFloats = int64_t(1) << 22;  // 16 MiB: b * h * s_q rows of delta
+hipError_t bwd_scratch(float** out);
 
 }  // namespace attn

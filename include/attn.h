@@ -49,7 +49,8 @@
  *   keeps no pointer after a call returns, and enqueues kernels asynchronously
  *   on `stream` (a hipStream_t; NULL means the default stream).  Calls are
  *   thread-safe: the only state is a per-device cache of the compute-unit count
- *   and architecture, filled once.  Buffers a call writes (O, LSE, partials,
+ *   and architecture, filled once (and the static buffer of attn_bwd_noalloc,
+ *   described there, for callers that cannot allocate).  Buffers a call writes (O, LSE, partials,
  *   dQ, dK, dV, delta) must not overlap one another or any buffer the call
  *   reads; this is not checked, and overlapping buffers give undefined results.
  *
@@ -82,7 +83,8 @@ typedef enum {
   ATTN_E_SCALE = -6,   /* softmax_scale is NaN or infinite */
   ATTN_E_SPLITS = -7,  /* num_splits outside [1, min(s_k, ATTN_MAX_SPLITS)] */
   ATTN_E_DEVICE = -8,  /* no HIP device, or the current device is not gfx950 */
-  ATTN_E_LAUNCH = -9   /* the kernel launch itself failed */
+  ATTN_E_LAUNCH = -9,  /* the kernel launch itself failed */
+  ATTN_E_SCRATCH = -10 /* attn_bwd_noalloc: b*h*s_q exceeds ATTN_BWD_SCRATCH_ROWS */
 } attn_status;
 
 typedef enum { ATTN_FP16 = 0, ATTN_BF16 = 1 } attn_dtype;
@@ -249,6 +251,20 @@ typedef struct {
 } attn_bwd_args;
 
 attn_status attn_bwd(const attn_bwd_args *args, void *stream);
+
+/* attn_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * checks, kernels and results, but args->delta is ignored (it may be NULL) and
+ * delta lives in a static device buffer of the library, ATTN_BWD_SCRATCH_ROWS
+ * fp32 values (16 MiB) that each device holds from its first call until the
+ * process ends.  The call allocates nothing; b*h*s_q must not exceed
+ * ATTN_BWD_SCRATCH_ROWS (else ATTN_E_SCRATCH, checked before anything is
+ * launched).  Every call on a device shares that device's buffer, which keeps
+ * the last call's contents; each call rewrites all of the delta it reads before
+ * reading it, so nothing needs clearing, but calls that overlap on one device
+ * (other streams or threads) race on the buffer and give undefined results. */
+#define ATTN_BWD_SCRATCH_ROWS (1 << 22)
+attn_status attn_bwd_noalloc(const attn_bwd_args *args, void *stream);
 
 /* Static, human-readable text for a status code. */
 const char *attn_status_str(int32_t status);

@@ -245,7 +245,7 @@ def test_combine_validation():
 
 
 def test_status_strings():
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         text = ea.status_str(code)
         assert text and text != "unknown status"
     assert ea.status_str(-42) == "unknown status"
@@ -351,6 +351,31 @@ BWD_CASES = [
 def test_bwd_validation(name, kw, code):
     a = _bwd(**kw)
     assert ea.lib().attn_bwd(ctypes.byref(a), None) == code
+
+
+NOALLOC_CASES = [c for c in BWD_CASES if "delta" not in c[0]]
+
+
+@pytest.mark.parametrize("name,kw,code", NOALLOC_CASES, ids=[c[0] for c in NOALLOC_CASES])
+def test_bwd_noalloc_validation(name, kw, code):
+    # the allocation-free backward runs the same checks (its delta is ignored)
+    a = _bwd(**kw)
+    assert ea.lib().attn_bwd_noalloc(ctypes.byref(a), None) == code
+
+
+def test_bwd_noalloc_scratch_limit_and_ignored_delta():
+    L = ea.lib()
+    assert L.attn_bwd_noalloc(None, None) == -1
+    # b*h*s_q above the static buffer (2^22 rows of delta): ATTN_E_SCRATCH before
+    # any device work; at the limit the host goes on to the device check
+    big = _bwd(b=2, h=4, s_q=(1 << 19) + 1, s_k=64)
+    assert L.attn_bwd_noalloc(ctypes.byref(big), None) == -10
+    import torch
+    if not torch.cuda.is_available():
+        at = _bwd(b=2, h=4, s_q=1 << 19, s_k=64, delta=None)
+        assert L.attn_bwd_noalloc(ctypes.byref(at), None) == -8
+        assert L.attn_bwd_noalloc(ctypes.byref(_bwd(delta=None)), None) == -8
+        assert L.attn_bwd(ctypes.byref(_bwd(delta=None)), None) == -1
 
 
 def test_bwd_null_args_and_no_device():
