@@ -123,8 +123,15 @@ void fwdp_kernel(const FwdParams p) {
   // has fp32's exponent range, where 2^64 keeps rebases rare.
   constexpr float PMAX = T_ == kFP16 ? 0x1p15f : 0x1p64f;
 
+  // QLDS: Q reaches its registers through LDS, loaded by the same direct-to-LDS
+  // loads as K and V and issued just before them, so that one memory round trip
+  // brings Q and the first tiles (loaded into registers, Q would be waited for
+  // on its own first).  Used where the extra NW * TILE bytes of LDS cost no
+  // occupancy: the 8-wave launch (one work-group per compute unit) and d = 16.
+  constexpr bool QLDS = NW == 8 || D == 16;
   __shared__ __attribute__((aligned(1024))) char kbuf[NBUF][TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf[NBUF][TILE];
+  __shared__ __attribute__((aligned(1024))) char qbuf[QLDS ? NW : 1][QLDS ? TILE : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -193,22 +200,38 @@ void fwdp_kernel(const FwdParams p) {
   // Rows past the end are zero; a negative scale is folded in by negating Q, a
   // zero scale by zeroing it.
   u32x4_t qf[RB][KK];
-  {
+  auto fix_q = [&](u32x4_t x) {
+    if (!row_ok || p.zero_q) return u32x4_t{0u, 0u, 0u, 0u};
+    return p.neg_q ? (x ^ 0x80008000u) : x;
+  };
+  if constexpr (QLDS) {
+    // This wave's 32 rows into qbuf[wave], chunks swizzled as in a K tile; rows
+    // past the end re-read the last row (zeroed once in registers).
+    const int rows = PACK ? p.g * p.s_q : p.s_q;
+#pragma unroll
+    for (int i = 0; i < TILE / 1024; ++i) {
+      const int slot = i * 64 + lane;
+      const int row = slot / NCH, pc = slot % NCH;
+      const int rw_ = min(q0 + wave * 32 + row, rows - 1);
+      const int pos = PACK ? rw_ % p.s_q : rw_;
+      const int head = PACK ? hk * p.g + rw_ / p.s_q : hg;
+      const unsigned short* src = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)pos * p.qs[1] +
+                                  (int64_t)head * p.qs[2] + (pc ^ Swz<D>::k(row)) * 8;
+      lds_dma16<false>((const void*)src, qbuf[wave] + i * 1024);
+    }
+  } else {
     const unsigned short* __restrict__ Qr =
         (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)my_i * p.qs[1] + (int64_t)my_h * p.qs[2];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4_t x = {0u, 0u, 0u, 0u};
-      if (row_ok && !p.zero_q) {
-        x = *(const u32x4_t*)(Qr + hi * 8 + kk * 16);
-        if (p.neg_q) x ^= 0x80008000u;
-      }
-      qf[0][kk] = x;
+      if (row_ok && !p.zero_q) x = *(const u32x4_t*)(Qr + hi * 8 + kk * 16);
+      qf[0][kk] = fix_q(x);
     }
+    // Wait for Q here, on every path: a load still pending where the key loop
+    // starts would make the compiler wait for all loads (vmcnt(0)) inside it.
+    __builtin_amdgcn_s_waitcnt(0);
   }
-  // Wait for Q here, on every path: a load still pending where the key loop
-  // starts would make the compiler wait for all loads (vmcnt(0)) inside it.
-  __builtin_amdgcn_s_waitcnt(0);
 
   f32x16_t o[CB][RB];
   float m[RB], l[RB];
@@ -390,10 +413,18 @@ void fwdp_kernel(const FwdParams p) {
     }
   }
   asm volatile("" ::: "memory");
-  if (full) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(WL + (P - 1) * PAIR));
+  // K_0 (and Q, issued before it) landed; a wave that loads no K/V has only Q
+  // in flight.
+  if (full && (NLW == NW || loader)) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(WL + (P - 1) * PAIR));
   else __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  if constexpr (QLDS) {
+    const char* qb = qbuf[wave];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[0][kk] = fix_q(*(const u32x4_t*)(qb + l32 * D * 2 + 16 * ((hi + 2 * kk) ^ Swz<D>::k(l32))));
+  }
   if (T > 0 && live) {
     u32x4_t kf[KK][NB];
     read_k(kbuf[0], kf);
@@ -526,15 +557,19 @@ void fwdp_kernel(const FwdParams p) {
 // ---------------------------------------------------------------------------
 // Launchers
 
+// Ring depth: 8 slots at d = 16 (1 KB tiles: a short head's whole K/V is in
+// flight after the prologue, and 8 work-groups still share a compute unit), else
+// kPrefillNBUF.
 template <int T_, int D, int NW, bool PACK, bool NT, bool PAGED, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwdp_t(const FwdParams& p, hipStream_t st) {
   constexpr int BM = NW * 32;
+  constexpr int NBUF = D == 16 ? 8 : kPrefillNBUF;
   FwdParams q = p;
   const int64_t rows = PACK ? (int64_t)p.g * p.s_q : p.s_q;
   const int64_t nh = PACK ? p.h / p.g : p.h;
   q.n_qt = (int)((rows + BM - 1) / BM);
   const int64_t grid = (int64_t)q.n_qt * p.b * nh * p.n_splits;
-  hipLaunchKernelGGL((fwdp_kernel<T_, D, kPrefillBN, NW, kPrefillNBUF, PACK, NT, PAGED, CAUSAL, SPLIT>),
+  hipLaunchKernelGGL((fwdp_kernel<T_, D, kPrefillBN, NW, NBUF, PACK, NT, PAGED, CAUSAL, SPLIT>),
                      dim3((unsigned)grid), dim3(NW * 64), 0, st, q);
   return hipGetLastError();
 }
