@@ -94,10 +94,14 @@ __global__ __launch_bounds__(kDecodeHeads * 64) void decode_kernel(const FwdPara
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
 
-  // Two register buffers, used alternately by a loop unrolled twice, so that the
-  // loads of one batch are in flight while the other is consumed (indices stay
-  // compile-time constants and the buffers stay in registers).
+  // ATTN_DECODE_NBUF (three) register buffers, used in turn by a loop unrolled
+  // as many times, so that the loads of the next batches are in flight while one
+  // is consumed (indices stay compile-time constants and the buffers stay in
+  // registers: one wave per SIMD leaves room for them).
   u32x4_t kb0[U], vb0[U], kb1[U], vb1[U];
+#if ATTN_DECODE_NBUF == 3
+  u32x4_t kb2[U], vb2[U];
+#endif
   auto load = [&](u32x4_t (&kb)[U], u32x4_t (&vb)[U], int j0) {
     int blk[3] = {0, 0, 0};
     int kb0 = 0;
@@ -155,6 +159,22 @@ __global__ __launch_bounds__(kDecodeHeads * 64) void decode_kernel(const FwdPara
     m = m_new;
   };
   constexpr int STEP = U * KPI;
+#if ATTN_DECODE_NBUF == 3
+  // three buffers, rotated by a loop unrolled three times: while one batch is
+  // consumed the next two are in flight
+  if (ws < we) load(kb0, vb0, ws);
+  if (ws + STEP < we) load(kb1, vb1, ws + STEP);
+  for (int j0 = ws; j0 < we; j0 += 3 * STEP) {
+    if (j0 + 2 * STEP < we) load(kb2, vb2, j0 + 2 * STEP);
+    consume(kb0, vb0, j0);
+    if (j0 + STEP >= we) break;
+    if (j0 + 3 * STEP < we) load(kb0, vb0, j0 + 3 * STEP);
+    consume(kb1, vb1, j0 + STEP);
+    if (j0 + 2 * STEP >= we) break;
+    if (j0 + 4 * STEP < we) load(kb1, vb1, j0 + 4 * STEP);
+    consume(kb2, vb2, j0 + 2 * STEP);
+  }
+#else
   if (ws < we) load(kb0, vb0, ws);
   for (int j0 = ws; j0 < we; j0 += 2 * STEP) {
     if (j0 + STEP < we) load(kb1, vb1, j0 + STEP);
@@ -163,6 +183,7 @@ __global__ __launch_bounds__(kDecodeHeads * 64) void decode_kernel(const FwdPara
     if (j0 + 2 * STEP < we) load(kb0, vb0, j0 + 2 * STEP);
     consume(kb1, vb1, j0 + STEP);
   }
+#endif
 
   // Merge the KPI slot states of the wave: butterfly over the slot index
   // (partner lane = lane ^ (LPH << k)), identical states in every slot after.
