@@ -334,6 +334,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "backward"], default="all")
     ap.add_argument("--no-small", action="store_true", help="skip the per-workload side table")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the clock, MFMA-loop and read-ceiling probes and the split sweep "
+                         "(counter runs that should see only the path's own kernels)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy five times (reference "
                          "kernel of known size for scaling HBM byte counters)")
@@ -440,7 +443,7 @@ def main():
         # heuristic): split-KV + combine between one event pair, caches flushed,
         # median of 10 passes per count.
         sweep = {}
-        for n in sorted({8, 16, 32, 48, 64, 96, 128, n_splits}):
+        for n in ([] if args.no_probes else sorted({8, 16, 32, 48, 64, 96, 128, n_splits})):
             op_n = torch.empty((n, wd.b, wd.h, wd.s_q, wd.d), dtype=torch.float32, device=dev)
             lp_n = torch.empty((n, wd.b, wd.h, wd.s_q), dtype=torch.float32, device=dev)
             ts = []
@@ -457,11 +460,11 @@ def main():
             del op_n, lp_n
         res["decode"] = dict(ms=d_med, ms_min=d_min, ms_mean=d_mean, splitkv_ms=s_ms, combine_ms=c_ms,
                              gbs=kvb / (d_med * 1e-3) / 1e9, kv_bytes=kvb, splits=n_splits, sweep=sweep,
-                             read=read_ceiling(torch, probe, kvb, flush, dev, E))
+                             read=None if args.no_probes else read_ceiling(torch, probe, kvb, flush, dev, E))
 
     # ---- what the device sustains: shader clock during back-to-back prefill
     # launches, and the power-limited MFMA ceiling of a register-only loop
-    if do_p:
+    if do_p and not args.no_probes:
         run_p = lambda: ea.attn_fwd(qp, kp, vp, wp.scale, wp.causal, out=Op, lse=Lp)  # noqa: E731
         res["prefill"]["sclk"] = shader_clock_mhz(torch, probe, run_p, 12, dev)
         res["prefill"]["mfma_ceiling"] = mfma_ceiling(torch, probe, dev, E)
@@ -603,8 +606,8 @@ def main():
                            "(attn_fwd_splitkv + attn_combine)" if do_d else ""),
             "b": wp.b, "s_q": wp.s_q, "s_k": wp.s_k, "h": wp.h, "d": wp.d, "causal": True,
         }
-        sclk, idle_mhz, peak_mhz = p["sclk"]
-        ceil = p["mfma_ceiling"]
+        sclk, idle_mhz, peak_mhz = p.get("sclk", (None, None, None))
+        ceil = p.get("mfma_ceiling", {"random_operands": None, "constant_operands": None})
         out["roofline"] = {
             "bound": "mfma", "achieved": round(p["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4),
@@ -617,7 +620,8 @@ def main():
             "frac_at_sclk": round(p["tflops"] / (PEAK_BF16_TFLOPS * sclk / peak_mhz), 4) if sclk else None,
             "mfma_loop_random_tflops": ceil["random_operands"],
             "mfma_loop_constant_tflops": ceil["constant_operands"],
-            "frac_of_random_mfma_loop": round(p["tflops"] / ceil["random_operands"], 4),
+            "frac_of_random_mfma_loop": (round(p["tflops"] / ceil["random_operands"], 4)
+                                         if ceil["random_operands"] else None),
         }
     if do_d:
         dd = res["decode"]
@@ -627,7 +631,7 @@ def main():
             "us_min": round(dd["ms_min"] * 1e3, 2), "us_mean": round(dd["ms_mean"] * 1e3, 2),
             "splitkv_us": round(dd["splitkv_ms"] * 1e3, 2), "combine_us": round(dd["combine_ms"] * 1e3, 2),
             "splits": dd["splits"], "frac_hbm": round(dd["gbs"] / PEAK_HBM_GBS, 4),
-            "read_ceiling": rd, "frac_of_read_ceiling": round(dd["gbs"] / rd["gbs"], 4),
+            "read_ceiling": rd, "frac_of_read_ceiling": round(dd["gbs"] / rd["gbs"], 4) if rd else None,
             "split_sweep_us": dd["sweep"],
         }
         rdl = {
