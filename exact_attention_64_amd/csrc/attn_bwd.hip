@@ -40,6 +40,9 @@
 #define ATTN_BWD_SMALL_NW 1  // waves per work-group of the dQ and dK/dV kernels at d <= 32 (b = 512, s = 150,
                              // d = 16: 0.305 ms with 4, 0.250 with 2, 0.240 with 1)
 #endif
+#ifndef ATTN_BWD_PF
+#define ATTN_BWD_PF 2  // LDS operand reads in flight ahead of the d = 128 kernels' products
+#endif
 #ifndef ATTN_BWD_DQ_NW
 #define ATTN_BWD_DQ_NW 8  // waves (32 query rows each) per work-group of the d = 128 dQ kernel
 #endif
@@ -79,18 +82,39 @@ template <int D> struct BTile {
 // logical chunk the swizzle maps there.  Rows at or past `nrows` re-read row
 // nrows - 1 (finite data; the kernels mask or discard what those rows produce).
 // The caller waits for the loads (s_waitcnt) before the barrier that publishes
-// the tile.
-template <int D, int NTH>
-__device__ __forceinline__ void dma_tile(const unsigned short* __restrict__ G, int64_t rs, int row0, int nrows,
-                                         int tid, int wave, char* lds) {
+// the tile.  TileOffs holds each load's element offset from the tile's first
+// row (row * rs + column), computed once, so that a tile lying inside the
+// sequence costs one 64-bit add per load.
+template <int D, int NTH> struct TileOffs {
+  static constexpr int N = BTile<D>::CHUNKS / NTH;
   static_assert(BTile<D>::CHUNKS % NTH == 0, "whole tiles per load round");
+  int64_t off[N];
+  __device__ __forceinline__ TileOffs(int64_t rs, int tid) {
 #pragma unroll
-  for (int i = 0; i < BTile<D>::CHUNKS / NTH; ++i) {
-    const int x = NTH * i + tid;
-    const int row = x / BTile<D>::NCH;
-    const int col = ((x % BTile<D>::NCH) ^ BTile<D>::sw(row)) * 8;
-    const int64_t r = min(row0 + row, nrows - 1);
-    lds_dma16<false>(G + r * rs + col, lds + (NTH * i + 64 * wave) * 16);
+    for (int i = 0; i < N; ++i) {
+      const int x = NTH * i + tid;
+      const int row = x / BTile<D>::NCH;
+      off[i] = (int64_t)row * rs + ((x % BTile<D>::NCH) ^ BTile<D>::sw(row)) * 8;
+    }
+  }
+};
+
+template <int D, int NTH>
+__device__ __forceinline__ void dma_tile(const TileOffs<D, NTH>& o, const unsigned short* __restrict__ G, int64_t rs,
+                                         int row0, int nrows, int tid, int wave, char* lds) {
+  if (row0 + 32 <= nrows) {  // wave-uniform
+    const unsigned short* B = G + (int64_t)row0 * rs;
+#pragma unroll
+    for (int i = 0; i < TileOffs<D, NTH>::N; ++i) lds_dma16<false>(B + o.off[i], lds + (NTH * i + 64 * wave) * 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < TileOffs<D, NTH>::N; ++i) {
+      const int x = NTH * i + tid;
+      const int row = x / BTile<D>::NCH;
+      const int col = ((x % BTile<D>::NCH) ^ BTile<D>::sw(row)) * 8;
+      const int64_t r = min(row0 + row, nrows - 1);
+      lds_dma16<false>(G + r * rs + col, lds + (NTH * i + 64 * wave) * 16);
+    }
   }
 }
 
@@ -149,20 +173,57 @@ __device__ __forceinline__ void store_cols(unsigned short* __restrict__ dst, con
 // that exp2(s*c - lse2) = 0 there.
 __device__ __forceinline__ float lse_log2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
 
+// A run of N matrix products use(i, frag) whose A operands come from LDS
+// (load(i)), with the reads PF products ahead of their use: the reads of
+// product i + PF are issued before product i, and a scheduling barrier keeps
+// them there.  Left to itself the compiler issues each read right before its
+// product, which then waits out the LDS latency.
+template <int I, int N, int PF> struct LdsPipe {
+  template <class Load, class Use>
+  static __device__ __forceinline__ void run(Load& load, Use& use, u32x4_t (&f)[PF + 1]) {
+    if constexpr (I < N) {
+      if constexpr (I + PF < N) f[(I + PF) % (PF + 1)] = load(I + PF);
+      __builtin_amdgcn_sched_barrier(0);
+      use(I, f[I % (PF + 1)]);
+      LdsPipe<I + 1, N, PF>::run(load, use, f);
+    }
+  }
+};
+template <int N, int PF, class Load, class Use>
+__device__ __forceinline__ void lds_pipeline(Load&& load, Use&& use) {
+  u32x4_t f[PF + 1];
+#pragma unroll
+  for (int i = 0; i < PF && i < N; ++i) f[i] = load(i);
+  LdsPipe<0, N, PF>::run(load, use, f);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // dQ: one work-group = NW waves x 32 query rows of one (b, query head) (8 waves
-// at d = 128, 4 at d = 64, one at d <= 32).
+// at d = 128, 4 at d = 64, one at d <= 32).  Per 32-key tile a wave runs three
+// stages: the products S^T and dP^T (matrix core), P and dS^T (vector ALU), and
+// the product dQ^T += K^T dS^T (matrix core).  With 8 waves two share each SIMD,
+// and the second half of the work-group (waves 4..7) runs half a tile behind
+// the first: after the barrier that ends step t it finishes tile t (P, dS^T,
+// dQ^T) and then forms S^T, dP^T of tile t + 1, while the first half forms,
+// finishes and multiplies tile t + 1 in that order.  So on each SIMD one wave's
+// vector work overlaps the other's products instead of both waves waiting on
+// the same stage.  The delay keeps three K/V tiles in LDS: the one the late
+// waves finish, the current one and the one in flight.
 template <int T_, int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
   using Tt = Ty<T_>;
   constexpr int KK = D / 16, CB = D >= 32 ? D / 32 : 1, BM = NW * 32, NTH = NW * 64;
-  __shared__ __attribute__((aligned(16))) char kbuf[2][BTile<D>::BYTES];
-  __shared__ __attribute__((aligned(16))) char vbuf[2][BTile<D>::BYTES];
+  constexpr bool SKEW = NW == 8;
+  constexpr int NB = SKEW ? 3 : 2;  // K/V tile buffers
+  __shared__ __attribute__((aligned(16))) char kbuf[NB][BTile<D>::BYTES];
+  __shared__ __attribute__((aligned(16))) char vbuf[NB][BTile<D>::BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool late = SKEW && wave >= NW / 2;  // wave-uniform
   const int n_qt = (p.s_q + BM - 1) / BM;
   // items (b*h, query tile) in head-major order, spread over the XCDs so that
   // the tiles of a head share one L2; causal: heaviest tiles first
@@ -219,59 +280,160 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
   const unsigned short* Vg = (const unsigned short*)p.v + (int64_t)bb * p.vs[0] + (int64_t)hk * p.vs[2];
   // K and V tiles go global -> LDS by direct-to-LDS loads; rows at or past k_hi
   // re-read row k_hi - 1 (finite data, masked scores)
-  auto issue = [&](int t, int buf) {
-    dma_tile<D, NTH>(Kg, p.ks[1], t * 32, k_hi, tid, wave, kbuf[buf]);
-    dma_tile<D, NTH>(Vg, p.vs[1], t * 32, k_hi, tid, wave, vbuf[buf]);
+  // Without the skew every thread loads part of both tiles at the start of a
+  // step.  With it, each half's 256 threads load one tile, spread over their
+  // products: the early half K between its S^T, dP^T products, the late half V
+  // between its dQ products (a wave that issues a burst of direct-to-LDS loads
+  // stalls until the memory pipeline takes them).
+  constexpr int NLD = SKEW ? NTH / 2 : NTH;
+  const int ltid = SKEW ? tid & (NLD - 1) : tid, lwave = SKEW ? wave & (NW / 2 - 1) : wave;
+  // with the skew a wave loads one of the two tiles: one set of offsets
+  const TileOffs<D, NLD> ko(SKEW && late ? p.vs[1] : p.ks[1], ltid), vo(p.vs[1], ltid);
+  auto load_k = [&](int t, int buf) __attribute__((always_inline)) {
+    dma_tile<D, NLD>(ko, Kg, p.ks[1], t * 32, k_hi, ltid, lwave, kbuf[buf]);
   };
-  if (T > 0) issue(0, 0);
+  auto load_v = [&](int t, int buf) __attribute__((always_inline)) {
+    dma_tile<D, NLD>(SKEW ? ko : vo, Vg, p.vs[1], t * 32, k_hi, ltid, lwave, vbuf[buf]);
+  };
+  auto nohook = []() __attribute__((always_inline)) {};
+  // S^T and dP^T of the tile in buffer buf, the two product chains interleaved
+  // so that one's latency hides the other's; dP^T starts from -delta, so the
+  // chain leaves dP - delta
+  auto products = [&](int buf, f32x16_t& s, f32x16_t& dp, auto&& hook) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = -dl;
+    }
+    if constexpr (SKEW) {
+      lds_pipeline<2 * KK, ATTN_BWD_PF>(
+          [&](int i) __attribute__((always_inline)) {
+            return frag_rows<D>(i % 2 == 0 ? kbuf[buf] : vbuf[buf], l32, hi, i / 2);
+          },
+          [&](int i, u32x4_t f) __attribute__((always_inline)) {
+            if (i % 2 == 0) s = Tt::mfma(f, qf[i / 2], s);
+            else dp = Tt::mfma(f, df[i / 2], dp);
+            if (i == KK - 1) hook();
+          });
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        s = Tt::mfma(frag_rows<D>(kbuf[buf], l32, hi, kk), qf[kk], s);
+        dp = Tt::mfma(frag_rows<D>(vbuf[buf], l32, hi, kk), df[kk], dp);
+      }
+    }
+  };
+  // P and dS^T of tile t (buffer buf) for this lane's row and its 16 keys (key of
+  // element r: k0 + (r/4)*8 + 4*hi + r%4), then dQ^T += K^T dS^T
+  auto finish = [&](int t, int buf, const f32x16_t& s, const f32x16_t& dp, auto&& hook) __attribute__((always_inline)) {
+    const int k0 = t * 32;
+    // masks only where a key of the tile is past the range or (causal) after the
+    // diagonal of the wave's first row; wave-uniform
+    const bool edge = k0 + 32 > k_hi || (CAUSAL && k0 + 31 > q0 + wave * 32 + off);
+    u32x4_t dsb[2];
+    if (edge) {
+#pragma unroll
+      for (int t16 = 0; t16 < 2; ++t16)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 8 * t16 + 2 * e + u;
+            const int key = k0 + (r / 4) * 8 + hi * 4 + (r % 4);
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+            if (key >= k_hi || (CAUSAL && key > my_i + off)) pr = 0.f;
+            x[u] = pr * dp[r];
+          }
+          dsb[t16][e] = Tt::pack2(x[0], x[1]);
+        }
+    } else {
+#pragma unroll
+      for (int t16 = 0; t16 < 2; ++t16)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 8 * t16 + 2 * e + u;
+            x[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2)) * dp[r];
+          }
+          dsb[t16][e] = Tt::pack2(x[0], x[1]);
+        }
+    }
+    if constexpr (SKEW) {
+      // consecutive products go to different accumulators
+      lds_pipeline<2 * CB, ATTN_BWD_PF>(
+          [&](int i) __attribute__((always_inline)) { return frag_cols<D>(kbuf[buf], lane, hi, i % CB, i / CB); },
+          [&](int i, u32x4_t f) __attribute__((always_inline)) {
+            acc[i % CB] = Tt::mfma(f, dsb[i / CB], acc[i % CB]);
+            if (i == CB - 1) hook();
+          });
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int t16 = 0; t16 < 2; ++t16)
+          acc[cb] = Tt::mfma(frag_cols<D>(kbuf[buf], lane, hi, cb, t16), dsb[t16], acc[cb]);
+    }
+  };
+
+  if (T > 0) {
+    if (!SKEW || !late) load_k(0, 0);
+    if (!SKEW || late) load_v(0, 0);
+  }
   // Every load issued so far (this lane's Q, dO, O, LSE and the first tile)
   // lands here, on every path: a load still pending where the loop starts would
   // make the compiler wait inside the loop for all loads, the next tile's included.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int t = 0; t < T; ++t) {
-    const int cur = t & 1;
-    const bool more = t + 1 < T;
-    if (more) issue(t + 1, cur ^ 1);  // that buffer was last read before the barrier ending step t - 1
-    const char* kb = kbuf[cur];
-    const char* vb = vbuf[cur];
-    f32x16_t s, dp;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-    // the two product chains interleaved, so that one's latency hides the other's
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      s = Tt::mfma(frag_rows<D>(kb, l32, hi, kk), qf[kk], s);
-      dp = Tt::mfma(frag_rows<D>(vb, l32, hi, kk), df[kk], dp);
-    }
-    // dS^T for this lane's row and its 16 keys (key of element r: k0 + (r/4)*8 + 4*hi + r%4).
-    const int k0 = t * 32;
-    // masks only where a key of the tile is past the range or (causal) after the
-    // diagonal of the wave's first row; wave-uniform
-    const bool edge = k0 + 32 > k_hi || (CAUSAL && k0 + 31 > q0 + wave * 32 + off);
-    u32x4_t dsb[2];
-#pragma unroll
-    for (int t16 = 0; t16 < 2; ++t16)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = 8 * t16 + 2 * e + u;
-          const int key = k0 + (r / 4) * 8 + hi * 4 + (r % 4);
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-          if (edge && (key >= k_hi || (CAUSAL && key > my_i + off))) pr = 0.f;
-          x[u] = pr * (dp[r] - dl);
+  // Step t: the step's work, during which tile t + 1 is loaded (into the buffer
+  // that held tile t + 1 - NB, finished before the barrier ending step t - 1);
+  // after the barrier tile t + 1 is in LDS.  Both halves pass the
+  // same T barriers.  The steps are unrolled over the NB buffers, so that every
+  // LDS address is a per-lane register plus an immediate offset.
+  f32x16_t s, dp;  // carried across the barrier by the late half
+  if (!late) {
+    for (int t0 = 0; t0 < T; t0 += NB)
+      static_for<0, NB>([&](auto R) __attribute__((always_inline)) {
+        constexpr int cur = decltype(R)::value, nxt = (cur + 1) % NB;
+        const int t = t0 + cur;
+        if (t < T) {
+          const bool more = t + 1 < T;
+          if constexpr (SKEW) {
+            products(cur, s, dp, [&]() __attribute__((always_inline)) { if (more) load_k(t + 1, nxt); });
+          } else {
+            if (more) {
+              load_k(t + 1, nxt);
+              load_v(t + 1, nxt);
+            }
+            products(cur, s, dp, nohook);
+          }
+          finish(t, cur, s, dp, nohook);
+          __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of tile t + 1 have landed
+          __syncthreads();
         }
-        dsb[t16][e] = Tt::pack2(x[0], x[1]);
-      }
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int t16 = 0; t16 < 2; ++t16) acc[cb] = Tt::mfma(frag_cols<D>(kb, lane, hi, cb, t16), dsb[t16], acc[cb]);
-    __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of tile t + 1 have landed
-    __syncthreads();
+      });
+  } else {
+    for (int t0 = 0; t0 < T; t0 += NB)
+      static_for<0, NB>([&](auto R) __attribute__((always_inline)) {
+        constexpr int cur = decltype(R)::value, nxt = (cur + 1) % NB, prv = (cur + NB - 1) % NB;
+        const int t = t0 + cur;
+        if (t < T) {
+          const bool more = t + 1 < T;
+          auto ld = [&]() __attribute__((always_inline)) { if (more) load_v(t + 1, nxt); };
+          if (t > 0) finish(t - 1, prv, s, dp, ld);
+          // nothing of the next products moves above this point: their
+          // accumulators reuse the registers of the finished tile's
+          __builtin_amdgcn_sched_barrier(0);
+          if (t == 0) products(cur, s, dp, ld);
+          else products(cur, s, dp, nohook);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+        }
+      });
+    if (T > 0) finish(T - 1, (T - 1) % NB, s, dp, nohook);
   }
 
   if (row_ok) {
@@ -346,7 +508,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv1_kernel(const BwdParams p) {
   // waits for these loads before the step's products.
   float lr = 0.f, dr = 0.f;
   bool row_in = false;
-  auto load_tile = [&](int t, int buf) {
+  const TileOffs<D, NW * 64> qo(p.qs[1], tid), oo(p.dos[1], tid);
+  auto load_tile = [&](int t, int buf) __attribute__((always_inline)) {
     const int hh = hk * p.g + t / nq;
     const int q0 = (qt0 + nq - 1 - t % nq) * 32;  // last tile first
     const int row = q0 + (tid & 31);
@@ -356,10 +519,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv1_kernel(const BwdParams p) {
     dr = p.delta[ri];
     const unsigned short* Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
     const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2];
-    dma_tile<D, NW * 64>(Qg, p.qs[1], q0, p.s_q, tid, wave, qbuf[buf]);
-    dma_tile<D, NW * 64>(Og, p.dos[1], q0, p.s_q, tid, wave, obuf[buf]);
+    dma_tile<D, NW * 64>(qo, Qg, p.qs[1], q0, p.s_q, tid, wave, qbuf[buf]);
+    dma_tile<D, NW * 64>(oo, Og, p.dos[1], q0, p.s_q, tid, wave, obuf[buf]);
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
     if (tid < 32) {
       lbuf[buf][tid] = row_in ? lse_log2(lr) : INFINITY;
       dbuf[buf][tid] = row_in ? dr : 0.f;
@@ -440,22 +603,25 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv1_kernel(const BwdParams p) {
 // 32-key block kb (waves kb and kb + 4, which share a SIMD):
 //   P-wave  (role 0): S = Q K^T, P = exp2(S*c - LSE*log2 e), hands P (fp32) to
 //                     its partner through LDS, and accumulates dV^T += dO^T P;
-//   dS-wave (role 1): dP = dO V^T, then, with the partner's P,
+//   dS-wave (role 1): dP - delta = dO V^T - delta, then, with the partner's P,
 //                     dS = P (dP - delta), and accumulates dK^T += Q^T dS.
 // So each wave holds one operand set (K or V of its keys) and one accumulator
-// set, two waves fit on a SIMD, and one wave's products overlap the other's
-// exponentials.  Per step: phase A (S or dP of both halves, two independent
-// product chains; the P-wave's exponentials and its P handoff), a barrier,
-// phase B (dV or dS and dK), the next tile's LDS stores, a barrier.
+// set, and two waves fit on a SIMD.  The dS-wave runs one tile behind: in step
+// t the P-wave forms S, P and dV of tile t, while the dS-wave finishes tile
+// t - 1 (dS from the P its partner left in step t - 1, then dK) and forms
+// dP - delta of tile t, which it carries across the step's one barrier.
+// Neither wave waits for the other inside a step, so one wave's exponentials
+// or dS overlap the other's products.  LDS holds three Q tiles (t - 1 for dK,
+// t, and t + 1 in flight), two dO tiles and two P buffers.
 template <int T_, int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
   using Tt = Ty<T_>;
   constexpr int KK = D / 16, CB = D >= 32 ? D / 32 : 1, BK = 128, NTH = 512, BQ = 64;
-  __shared__ __attribute__((aligned(16))) char qbuf[2][2][BTile<D>::BYTES];  // [buffer][half]
+  __shared__ __attribute__((aligned(16))) char qbuf[3][2][BTile<D>::BYTES];  // [buffer][half]
   __shared__ __attribute__((aligned(16))) char obuf[2][2][BTile<D>::BYTES];
   __shared__ __attribute__((aligned(16))) float lbuf[2][BQ];
-  __shared__ __attribute__((aligned(16))) float dbuf[2][BQ];
-  __shared__ __attribute__((aligned(16))) f32x4_t xbuf[2][4][4][64];  // [half][key block][r4][lane]: P
+  __shared__ __attribute__((aligned(16))) float dbuf[2][BQ];  // -delta
+  __shared__ __attribute__((aligned(16))) f32x4_t xbuf[2][2][4][4][64];  // [buffer][half][key block][r4][lane]: P
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -498,112 +664,188 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
+  // first row of tile t (tiles of a query head are walked last first)
+  auto tile_q0 = [&](int t) __attribute__((always_inline)) { return (qt0 + nq - 1 - t % nq) * BQ; };
   // Q and dO tiles go global -> LDS by direct-to-LDS loads (rows past s_q re-read
-  // row s_q - 1: finite data, and their LSE is +inf, so P = 0).
-  // LSE and delta of staged row tid % 64, loaded by every lane without a branch
-  // (the row index is clamped) and converted only when stored, so that nothing
-  // waits for these loads before the step's products.
+  // row s_q - 1: finite data, and their LSE is +inf, so P = 0).  Wave 0 also
+  // loads LSE and delta of the tile's row q0 + lane (row index clamped, no
+  // branch) and converts them only when it stores them at the end of the step,
+  // so that nothing waits for these loads before the step's products.
   float lr = 0.f, dr = 0.f;
   bool row_in = false;
-  auto load_tile = [&](int t, int buf) {
+  // The loads of tile t + 1 are spread over the products of step t: the P-waves
+  // load Q between their S products, the dS-waves dO between their dP products
+  // (a wave that issues a burst of direct-to-LDS loads stalls until the memory
+  // pipeline takes them).  Each role's 256 threads cover a whole tile.
+  constexpr int NLD = 256;
+  const int ltid = tid & (NLD - 1), lwave = wave & 3;
+  const TileOffs<D, NLD> qo(p.qs[1], ltid), oo(p.dos[1], ltid);
+  auto load_rows = [&](int t) __attribute__((always_inline)) {  // wave 0: LSE, delta of tile t
     const int hh = hk * p.g + t / nq;
-    const int q0 = (qt0 + nq - 1 - t % nq) * BQ;  // last tile first
-    const int row = q0 + (tid & (BQ - 1));
+    const int row = tile_q0(t) + lane;
     row_in = row < p.s_q;
     const int64_t ri = ((int64_t)bb * p.h + hh) * p.s_q + min(row, p.s_q - 1);
     lr = p.lse[ri];
     dr = p.delta[ri];
-    const unsigned short* Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
-    const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2];
+  };
+  // part j of tile t: Q (j = 0, 1) or dO (j = 2, 3), half j % 2, into qbuf[qb] / obuf[ob]
+  auto load_part = [&](int t, int j, int qb, int ob) __attribute__((always_inline)) {
+    const int hh = hk * p.g + t / nq;
+    const int r0 = tile_q0(t) + 32 * (j % 2);
+    if (j < 2) {
+      const unsigned short* Qg = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)hh * p.qs[2];
+      dma_tile<D, NLD>(qo, Qg, p.qs[1], r0, p.s_q, ltid, lwave, qbuf[qb][j % 2]);
+    } else {
+      const unsigned short* Og = (const unsigned short*)p.dout + (int64_t)bb * p.dos[0] + (int64_t)hh * p.dos[2];
+      dma_tile<D, NLD>(oo, Og, p.dos[1], r0, p.s_q, ltid, lwave, obuf[ob][j % 2]);
+    }
+  };
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    if (wave == 0) {
+      lbuf[buf][lane] = row_in ? lse_log2(lr) : INFINITY;
+      dbuf[buf][lane] = row_in ? -dr : 0.f;  // -delta
+    }
+  };
+
+  // P-wave, tile t (Q in qbuf[qc]; dO, LSE and P in slot ob = t % 2 of obuf,
+  // lbuf and xbuf): S of both halves for this lane's key and its 16 rows of each
+  // half (row of element r of half hf: q0 + 32*hf + (r/4)*8 + 4*hi + r%4), P into
+  // xbuf, then dV^T += dO^T P.
+  auto p_step = [&](int t, int qc, int ob, bool more, int qn) __attribute__((always_inline)) {
+    const int q0 = tile_q0(t);
+    f32x16_t sc[2];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      dma_tile<D, NTH>(Qg, p.qs[1], q0 + 32 * hf, p.s_q, tid, wave, qbuf[buf][hf]);
-      dma_tile<D, NTH>(Og, p.dos[1], q0 + 32 * hf, p.s_q, tid, wave, obuf[buf][hf]);
-    }
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[hf][r] = 0.f;
+    // the two Q halves of tile t + 1 go out after products KK / 2 - 1 and 3 KK / 2 - 1
+    lds_pipeline<2 * KK, ATTN_BWD_PF>(
+        [&](int i) __attribute__((always_inline)) { return frag_rows<D>(qbuf[qc][i % 2], l32, hi, i / 2); },
+        [&](int i, u32x4_t f) __attribute__((always_inline)) {
+          sc[i % 2] = Tt::mfma(f, opnd[i / 2], sc[i % 2]);
+          if (more && i % KK == KK / 2 - 1) load_part(t + 1, i / KK, qn, 0);
+        });
+    u32x4_t bop[2][2];  // [half][chunk]: B operand of dV^T += dO^T P
+    // causal mask only where the wave's last key is after the diagonal of the
+    // tile's first row; wave-uniform
+    const bool diag = CAUSAL && k0 + kb * 32 + 31 > q0 + off;
+    auto probs = [&](auto MASK) __attribute__((always_inline)) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4_t l4 = *(const f32x4_t*)(&lbuf[ob][32 * hf + r4 * 8 + hi * 4]);
+          f32x4_t pr;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            pr[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hf][4 * r4 + u], c, -l4[u]));
+            if (decltype(MASK)::value && my_j > q0 + 32 * hf + r4 * 8 + hi * 4 + u + off) pr[u] = 0.f;
+          }
+          xbuf[ob][hf][kb][r4][lane] = pr;
+          bop[hf][r4 / 2][2 * (r4 % 2)] = Tt::pack2(pr[0], pr[1]);
+          bop[hf][r4 / 2][2 * (r4 % 2) + 1] = Tt::pack2(pr[2], pr[3]);
+        }
+    };
+    if (diag) probs(IC<1>{});
+    else probs(IC<0>{});
+    // product i: half i / (2 CB), chunk (i / CB) % 2, accumulator i % CB
+    lds_pipeline<4 * CB, ATTN_BWD_PF>(
+        [&](int i) __attribute__((always_inline)) {
+          return frag_cols<D>(obuf[ob][i / (2 * CB)], lane, hi, i % CB, (i / CB) % 2);
+        },
+        [&](int i, u32x4_t f) __attribute__((always_inline)) {
+          acc[i % CB] = Tt::mfma(f, bop[i / (2 * CB)][(i / CB) % 2], acc[i % CB]);
+        });
   };
-  auto store_tile = [&](int buf) {
-    if (tid < BQ) {
-      lbuf[buf][tid] = row_in ? lse_log2(lr) : INFINITY;
-      dbuf[buf][tid] = row_in ? dr : 0.f;
-    }
+  // dS-wave: dP - delta of a tile (dO and -delta in slot ob of obuf and dbuf), the
+  // accumulators starting from -delta of their rows
+  auto d_products = [&](int t, int ob, f32x16_t (&dpm)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4_t d4 = *(const f32x4_t*)(&dbuf[ob][32 * hf + r4 * 8 + hi * 4]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dpm[hf][4 * r4 + u] = d4[u];
+      }
+    // the two dO halves of tile t + 1 go out after products KK / 2 - 1 and 3 KK / 2 - 1
+    const bool more = t + 1 < T;
+    lds_pipeline<2 * KK, ATTN_BWD_PF>(
+        [&](int i) __attribute__((always_inline)) { return frag_rows<D>(obuf[ob][i % 2], l32, hi, i / 2); },
+        [&](int i, u32x4_t f) __attribute__((always_inline)) {
+          dpm[i % 2] = Tt::mfma(f, opnd[i / 2], dpm[i % 2]);
+          if (more && i % KK == KK / 2 - 1) load_part(t + 1, 2 + i / KK, 0, ob ^ 1);
+        });
   };
+  // dS-wave: dS = P (dP - delta) of a tile (P in xbuf[xb], Q in qbuf[qc]), then
+  // dK^T += Q^T dS
+  auto d_finish = [&](int qc, int xb, const f32x16_t (&dpm)[2]) __attribute__((always_inline)) {
+    u32x4_t bop[2][2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4_t pr = xbuf[xb][hf][kb][r4][lane];
+        bop[hf][r4 / 2][2 * (r4 % 2)] = Tt::pack2(pr[0] * dpm[hf][4 * r4], pr[1] * dpm[hf][4 * r4 + 1]);
+        bop[hf][r4 / 2][2 * (r4 % 2) + 1] = Tt::pack2(pr[2] * dpm[hf][4 * r4 + 2], pr[3] * dpm[hf][4 * r4 + 3]);
+      }
+    lds_pipeline<4 * CB, ATTN_BWD_PF>(
+        [&](int i) __attribute__((always_inline)) {
+          return frag_cols<D>(qbuf[qc][i / (2 * CB)], lane, hi, i % CB, (i / CB) % 2);
+        },
+        [&](int i, u32x4_t f) __attribute__((always_inline)) {
+          acc[i % CB] = Tt::mfma(f, bop[i / (2 * CB)][(i / CB) % 2], acc[i % CB]);
+        });
+  };
+
   if (T > 0) {
-    load_tile(0, 0);
+    if (wave == 0) load_rows(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) load_part(0, 2 * role + j, 0, 0);
     store_tile(0);
   }
   // K or V and the first tile land here, on every path (see the dQ kernel).
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int t = 0; t < T; ++t) {
-    const int cur = t & 1;
-    const bool more = t + 1 < T;
-    if (more) load_tile(t + 1, cur ^ 1);  // that buffer was last read before the barrier ending step t - 1
-    const int q0 = (qt0 + nq - 1 - t % nq) * BQ;  // last tile first
-    // Phase A: S (P-wave) or dP (dS-wave) of both halves for this lane's key and
-    // its 16 rows of each half (row of element r of half hf:
-    // q0 + 32*hf + (r/4)*8 + 4*hi + r%4).
-    f32x16_t sc[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[hf][r] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        sc[hf] = Tt::mfma(frag_rows<D>(role == 0 ? qbuf[cur][hf] : obuf[cur][hf], l32, hi, kk), opnd[kk], sc[hf]);
-    u32x4_t bop[2][2];  // [half][chunk]: B operand of phase B, P (P-wave) or dS (dS-wave)
-    // causal mask only where the wave's last key is after the diagonal of the
-    // tile's first row; wave-uniform
-    const bool diag = k0 + kb * 32 + 31 > q0 + off;
-    if (role == 0) {
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4_t l4 = *(const f32x4_t*)(&lbuf[cur][32 * hf + r4 * 8 + hi * 4]);
-          f32x4_t pr;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int row = q0 + 32 * hf + r4 * 8 + hi * 4 + u;
-            float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hf][4 * r4 + u], c, -l4[u]));
-            if (CAUSAL && diag && my_j > row + off) x = 0.f;
-            pr[u] = x;
-          }
-          xbuf[hf][kb][r4][lane] = pr;
-          bop[hf][r4 / 2][2 * (r4 % 2)] = Tt::pack2(pr[0], pr[1]);
-          bop[hf][r4 / 2][2 * (r4 % 2) + 1] = Tt::pack2(pr[2], pr[3]);
+  // Step t: the step's work, during which tile t + 1 is loaded (Q into the
+  // buffer that held tile t - 2, dO into the one that held t - 1: both finished
+  // before the barrier ending step t - 1) and wave 0 stores LSE and delta of
+  // tile t + 1; after the barrier tile t + 1 is in LDS.  Both roles pass the same
+  // T barriers.  The steps are unrolled over the period of the buffer rings (3
+  // Q buffers, 2 of the rest), so that every LDS address is a per-lane register
+  // plus an immediate offset.
+  if (role == 0) {
+    for (int t0 = 0; t0 < T; t0 += 6)
+      static_for<0, 6>([&](auto R) __attribute__((always_inline)) {
+        constexpr int r = decltype(R)::value, qc = r % 3, ob = r % 2;
+        const int t = t0 + r;
+        if (t < T) {
+          const bool more = t + 1 < T;
+          if (more && wave == 0) load_rows(t + 1);
+          p_step(t, qc, ob, more, (r + 1) % 3);
+          if (more) store_tile(ob ^ 1);
+          __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of tile t + 1 have landed
+          __syncthreads();
         }
-    }
-    __syncthreads();
-    // Phase B
-    if (role == 1) {
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4_t pr = xbuf[hf][kb][r4][lane];
-          const f32x4_t d4 = *(const f32x4_t*)(&dbuf[cur][32 * hf + r4 * 8 + hi * 4]);
-          float ds[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) ds[u] = pr[u] * (sc[hf][4 * r4 + u] - d4[u]);
-          bop[hf][r4 / 2][2 * (r4 % 2)] = Tt::pack2(ds[0], ds[1]);
-          bop[hf][r4 / 2][2 * (r4 % 2) + 1] = Tt::pack2(ds[2], ds[3]);
+      });
+  } else {
+    f32x16_t dpm[2];  // dP - delta of the last tile formed, carried across the barrier
+    for (int t0 = 0; t0 < T; t0 += 6)
+      static_for<0, 6>([&](auto R) __attribute__((always_inline)) {
+        constexpr int r = decltype(R)::value, ob = r % 2;
+        const int t = t0 + r;
+        if (t < T) {
+          if (t > 0) d_finish((r + 2) % 3, ob ^ 1, dpm);  // tile t - 1
+          // nothing of the next products moves above this point: their
+          // accumulators reuse the registers of the finished tile's
+          __builtin_amdgcn_sched_barrier(0);
+          d_products(t, ob, dpm);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
         }
-    }
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const char* tb = role == 0 ? obuf[cur][hf] : qbuf[cur][hf];  // dO^T for dV, Q^T for dK
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int t16 = 0; t16 < 2; ++t16)
-          acc[cb] = Tt::mfma(frag_cols<D>(tb, lane, hi, cb, t16), bop[hf][t16], acc[cb]);
-    }
-    if (more) store_tile(cur ^ 1);
-    __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of tile t + 1 have landed
-    __syncthreads();
+      });
+    if (T > 0) d_finish((T - 1) % 3, (T - 1) & 1, dpm);
   }
 
   if (key_ok) {

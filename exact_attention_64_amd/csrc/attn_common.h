@@ -74,6 +74,16 @@ __device__ __forceinline__ int xcd_item(int id, int n) {
   return x * q + min(x, r) + id / 8;
 }
 
+// A compile-time integer, and f(IC<I>{}), ..., f(IC<N - 1>{}) unrolled.
+template <int N> struct IC { static constexpr int value = N; };
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IC<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // s_waitcnt immediate (gfx9 encoding): vmcnt(n), lgkmcnt(0), expcnt untouched.
 constexpr int vmcnt_lgkm0(int n) { return (n & 0xF) | (((n >> 4) & 0x3) << 14) | (0x7 << 4); }
 

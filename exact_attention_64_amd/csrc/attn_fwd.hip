@@ -68,16 +68,6 @@ template <int D> struct Swz {
 // rounded P stays finite, m never falls below the running maximum by more than
 // log2(PMAX), and no exponent overflows; rows whose scores fall far below m only
 // lose terms that are negligible against the row's maximum.
-template <int N> struct IC { static constexpr int value = N; };
-
-// f(IC<I>{}), ..., f(IC<N - 1>{}), unrolled at compile time.
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(IC<I>{});
-    static_for<I + 1, N>(f);
-  }
-}
 
 // PACK (query heads sharing a K/V head, few query rows): a work-group covers one
 // (batch, K/V head) and its g * s_q query rows, row r being query head
