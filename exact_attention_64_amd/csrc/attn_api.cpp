@@ -342,7 +342,12 @@ attn_status attn_num_splits_paged(int64_t b, int64_t h, int64_t h_kv, int64_t s_
   if (st != ATTN_OK) return st;
   if (!info.gfx950 || info.cus < 1) return ATTN_E_DEVICE;
   const int64_t g = h_kv > 0 ? h / h_kv : 1;
-  *n_out = (int32_t)splits_for_work(attn::fwd_groups_per_split(b, h, g, s_q, (int)d), max_seqlen_k, info.cus);
+  // Packed groups over a paged cache: two work-groups per compute unit, since the
+  // block ids each tile needs are scalar loads in the key stream's critical path
+  // (b = 8, h = 48, h_kv = 8, 4096 keys in 64-key blocks: 8 splits ran 8-11%
+  // faster than 4, for 1 and 4 query rows).
+  const int64_t cus = attn::fwd_packed(g, s_q, (int)d) ? 2 * (int64_t)info.cus : info.cus;
+  *n_out = (int32_t)splits_for_work(attn::fwd_groups_per_split(b, h, g, s_q, (int)d), max_seqlen_k, cus);
   return ATTN_OK;
 }
 

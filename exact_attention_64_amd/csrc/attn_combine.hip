@@ -99,15 +99,93 @@ __global__ __launch_bounds__(64) void combine_kernel(const CombineParams p) {
   }
 }
 
+// The same reduction for many rows (multi-token decode, many heads): one wave
+// covers RPW = 256 / D whole rows, CPR = D / 4 lanes per row, each lane 4
+// columns, so a split's slice of a row is one contiguous read of 4 D bytes and
+// no lane idles for want of splits.  Three passes over the row's splits: the
+// maximum of the LSE_i (lane c takes splits c, c + CPR, ...), the sum of
+// exponentials (same lanes), then O += exp(LSE_i - LSE) * O_i over i in
+// increasing order, the O_i loads issued eight at a time.  Deterministic.
+template <int T_, int D>
+__global__ __launch_bounds__(64) void combine_rows_kernel(const CombineParams p) {
+  using Tt = Ty<T_>;
+  constexpr int CPR = D / 4, RPW = 64 / CPR, CH = 8;
+  const int lane = threadIdx.x, c = lane % CPR;
+  const int64_t rows = (int64_t)p.b * p.h * p.s_q;
+  const int64_t row = (int64_t)blockIdx.x * RPW + lane / CPR;
+  const bool ok = row < rows;
+  const int64_t rw = ok ? row : rows - 1;  // loads stay in bounds
+  const int n = p.n_splits;                // <= kMaxSplits
+  const float* __restrict__ lp = p.lse_part + rw;
+  const float* __restrict__ op = p.o_part + rw * D + c * 4;
+
+  float mx = -INFINITY;
+  for (int i = c; i < n; i += CPR) mx = fmaxf(mx, lp[(int64_t)i * rows]);
+#pragma unroll
+  for (int o = 1; o < CPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float Ms = mx == -INFINITY ? 0.f : mx;
+  float e = 0.f;
+  for (int i = c; i < n; i += CPR) {
+    const float l = lp[(int64_t)i * rows];
+    e += l == -INFINITY ? 0.f : expf(l - Ms);
+  }
+#pragma unroll
+  for (int o = 1; o < CPR; o <<= 1) e += __shfl_xor(e, o);
+  const bool has = mx != -INFINITY && e > 0.f;
+  const float lse = has ? Ms + logf(e) : -INFINITY;
+
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (has) {
+    for (int i0 = 0; i0 < n; i0 += CH) {
+      f32x4_t x[CH];
+      float lw[CH];
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const int i = i0 + u;
+        const bool in = i < n;
+        x[u] = in ? *(const f32x4_t*)(op + (int64_t)i * rows * D) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        lw[u] = in ? lp[(int64_t)i * rows] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < CH; ++u)
+        if (lw[u] != -INFINITY) acc += expf(lw[u] - lse) * x[u];
+    }
+  }
+  if (ok) {
+    const int i = (int)(row % p.s_q);
+    const int64_t bh = row / p.s_q;
+    const int bb = (int)(bh / p.h), hh = (int)(bh % p.h);
+    unsigned short* o = (unsigned short*)p.o + (int64_t)bb * p.os[0] + (int64_t)i * p.os[1] + (int64_t)hh * p.os[2] +
+                        c * 4;
+    u32x2_t w = {Tt::pack2(acc[0], acc[1]), Tt::pack2(acc[2], acc[3])};
+    *(u32x2_t*)o = w;
+    if (c == 0 && p.lse) p.lse[row] = lse;
+  }
+}
+
+// Few rows (single-token decode: b * h rows): the column-sliced kernel, which
+// spreads a row over d / 16 waves and its splits over the lanes; from
+// kCombineRowsMin rows on, the row kernel.
+constexpr int64_t kCombineRowsMin = 128;
+
+template <int T_, int D>
+static void launch_combine_d(const CombineParams& p, int64_t rows, hipStream_t st) {
+  if (rows >= kCombineRowsMin) {
+    constexpr int RPW = 256 / D;
+    hipLaunchKernelGGL((combine_rows_kernel<T_, D>), dim3((unsigned)((rows + RPW - 1) / RPW)), dim3(64), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<T_, D>), dim3((unsigned)(rows * (D / kCombineCols))), dim3(64), 0, st, p);
+  }
+}
+
 template <int T_>
 static hipError_t launch_combine_t(const CombineParams& p, hipStream_t st) {
   const int64_t rows = (int64_t)p.b * p.h * p.s_q;
-  const dim3 grid((unsigned)(rows * (p.d / kCombineCols)));
   switch (p.d) {
-    case 16: hipLaunchKernelGGL((combine_kernel<T_, 16>), grid, dim3(64), 0, st, p); break;
-    case 32: hipLaunchKernelGGL((combine_kernel<T_, 32>), grid, dim3(64), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((combine_kernel<T_, 64>), grid, dim3(64), 0, st, p); break;
-    default: hipLaunchKernelGGL((combine_kernel<T_, 128>), grid, dim3(64), 0, st, p); break;
+    case 16: launch_combine_d<T_, 16>(p, rows, st); break;
+    case 32: launch_combine_d<T_, 32>(p, rows, st); break;
+    case 64: launch_combine_d<T_, 64>(p, rows, st); break;
+    default: launch_combine_d<T_, 128>(p, rows, st); break;
   }
   return hipGetLastError();
 }

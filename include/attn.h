@@ -211,7 +211,9 @@ attn_status attn_fwd_splitkv_paged(const attn_paged_args *args, int32_t num_spli
                                    float *o_part, float *lse_part, void *stream);
 
 /* Split count for attn_fwd_splitkv_paged: the rule of attn_num_splits_kv with
- * s_k = max_seqlen_k (the paged cache runs the same kernels and work-groups). */
+ * s_k = max_seqlen_k (the paged cache runs the same kernels and work-groups),
+ * except that packed query-head groups (h_kv < h, few query rows) aim at two
+ * work-groups per compute unit instead of one. */
 attn_status attn_num_splits_paged(int64_t b, int64_t h, int64_t h_kv, int64_t s_q,
                                   int64_t max_seqlen_k, int64_t d, int device, int32_t *n_out);
 
