@@ -44,7 +44,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCES = ["exact_attention_64_amd/csrc/attn_fwd.hip", "exact_attention_64_amd/csrc/attn_decode.hip",
-                  "exact_attention_64_amd/csrc/attn_combine.hip", "exact_attention_64_amd/csrc/attn_common.h",
+                  "exact_attention_64_amd/csrc/attn_combine.hip", "exact_attention_64_amd/csrc/attn_small.hip",
+                  "exact_attention_64_amd/csrc/attn_common.h", "exact_attention_64_amd/csrc/attn_tile.h",
                   "exact_attention_64_amd/csrc/attn_internal.h"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.md")
 CPU_ROWS_PER_HEAD = 4096  # seeded query rows per head in the CPU-baseline sample (~12 s of oracle work)

@@ -28,6 +28,7 @@ SOURCES = [("attn_api.cpp", "attn_api", []),
              for t in (0, 1) for c in (0, 1) for g in (0, 1)],
            ("attn_decode.hip", "attn_decode", []),
            ("attn_combine.hip", "attn_combine", []),
+           ("attn_small.hip", "attn_small", []),
            ("attn_bwd.hip", "attn_bwd", [])]
 
 # Packed fp32 VALU instructions are switched off for every HIP translation unit.

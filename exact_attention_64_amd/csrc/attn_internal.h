@@ -141,13 +141,22 @@ inline hipError_t launch_prefill(const FwdParams& p, int dtype, bool causal, boo
 }
 // One-row decode kernel (s_q == 1).
 hipError_t launch_decode(const FwdParams& p, int dtype, bool split, hipStream_t st);
-// One of the two above: the decode kernel for one query row unless query heads
-// share K/V heads (then the packed prefill kernel reads each K/V tile once per
-// group).  With one query row the bottom-right causal mask hides nothing, so the
-// causal flag does not matter there.
+// One of the kernels above: the decode kernel for one query row unless query
+// heads share K/V heads (then the packed prefill kernel reads each K/V tile once
+// per group; with one query row the bottom-right causal mask hides nothing, so
+// the causal flag does not matter there), the small-head kernel where it
+// applies, else the prefill kernel.
+// Persistent small-head forward (attn_small.hip): d <= 32 and both sequence
+// lengths at most kSmallMaxSeq, fused (not split), contiguous K/V.
+constexpr int kSmallMaxSeq = 256;
+inline bool small_fwd_ok(const FwdParams& p) {
+  return p.d <= 32 && p.s_q <= kSmallMaxSeq && p.s_k <= kSmallMaxSeq && (int64_t)p.b * p.h <= 0x7fffffff;
+}
+hipError_t launch_small(const FwdParams& p, int dtype, bool causal, hipStream_t st);
 inline hipError_t launch_fwd(const FwdParams& p, int dtype, bool causal, bool split, hipStream_t st) {
-  return p.s_q == 1 && !fwd_packed(p.g, p.s_q, p.d) ? launch_decode(p, dtype, split, st)
-                                                     : launch_prefill(p, dtype, causal, split, st);
+  if (p.s_q == 1 && !fwd_packed(p.g, p.s_q, p.d)) return launch_decode(p, dtype, split, st);
+  if (!split && !p.block_table && small_fwd_ok(p)) return launch_small(p, dtype, causal, st);
+  return launch_prefill(p, dtype, causal, split, st);
 }
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t st);
 // Backward: dQ (which also writes delta), then dK/dV, enqueued in that order on `st`.

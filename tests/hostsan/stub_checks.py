@@ -68,6 +68,23 @@ def test_decode_and_split_routing():
     assert L.stub_last_kind() == 1 and field("g") == 4 and field("n_splits") == 3
 
 
+def test_small_head_routing():
+    L = stub()
+    # d <= 32 with both lengths <= 256: the persistent small-head kernel; longer
+    # sequences, one query row or a split pass: the other kernels
+    for d, s_q, s_k, kind in ((16, 150, 150, 5), (32, 256, 256, 5), (16, 257, 100, 1), (32, 100, 257, 1),
+                              (64, 100, 100, 1), (16, 1, 100, 2)):
+        a = fwd_args(s_q=s_q, s_k=s_k, d=d, q_stride=_lib.I64x3(s_q * 4 * d, 4 * d, d),
+                     k_stride=_lib.I64x3(s_k * 4 * d, 4 * d, d), v_stride=_lib.I64x3(s_k * 4 * d, 4 * d, d),
+                     o_stride=_lib.I64x3(s_q * 4 * d, 4 * d, d))
+        assert L.attn_fwd(ctypes.byref(a), None) == 0 and L.stub_last_kind() == kind, (d, s_q, s_k)
+        if kind == 5:
+            assert field("s_q") == s_q and field("s_k") == s_k and field("split") == 0
+    a = fwd_args(s_q=150, s_k=150, d=16, q_stride=_lib.I64x3(150 * 64, 64, 16), k_stride=_lib.I64x3(150 * 64, 64, 16),
+                 v_stride=_lib.I64x3(150 * 64, 64, 16), o_stride=_lib.I64x3(150 * 64, 64, 16))
+    assert L.attn_fwd_splitkv(ctypes.byref(a), 3, FAKE, FAKE, None) == 0 and L.stub_last_kind() == 1
+
+
 def test_combine_params():
     L = stub()
     st = _lib.I64x3(5 * 16 * 64, 16 * 64, 64)

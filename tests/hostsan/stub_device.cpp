@@ -64,6 +64,15 @@ hipError_t launch_decode(const FwdParams& p, int dtype, bool split, hipStream_t)
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_small(const FwdParams& p, int dtype, bool causal, hipStream_t) {
+  g_fwd = p;
+  g_kind = 5;
+  g_dtype = dtype;
+  g_causal = causal;
+  g_split = 0;
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t) {
   g_comb = p;
   g_kind = 3;
@@ -95,7 +104,7 @@ extern "C" double stub_field(const char* name) {
   if (n == "dtype") return g_dtype;
   if (n == "causal") return g_causal;
   if (n == "split") return g_split;
-  if (g_kind == 1 || g_kind == 2) {
+  if (g_kind == 1 || g_kind == 2 || g_kind == 5) {
     const attn::FwdParams& p = g_fwd;
     if (n == "b") return p.b;
     if (n == "h") return p.h;

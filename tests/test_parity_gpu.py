@@ -437,6 +437,46 @@ def test_combine_identical_splits_adds_ln2():
     assert (O2 == 0).all() and torch.isinf(L2).all() and (L2 < 0).all()
 
 
+SMALL_HEAD_CASES = [
+    # dtype, b, s_q, s_k, h, h_kv, d, scale: the persistent small-head kernel
+    # (d <= 32, both lengths <= 256); thousands of (b, h) items, so that every
+    # work-group loops over several of them through its two LDS buffers
+    ("fp16", 96, 40, 70, 32, 32, 16, None),
+    ("bf16", 64, 33, 64, 48, 16, 32, None),     # shared K/V heads, a ragged query block
+    ("bf16", 4, 256, 256, 8, 8, 32, None),      # eight key tiles and eight waves
+    ("fp16", 8, 100, 60, 16, 16, 16, None),     # s_q > s_k: causal rows that see no key
+    ("fp16", 32, 50, 31, 8, 8, 16, 0.0),        # scale 0: uniform weights over visible keys
+    ("bf16", 32, 77, 45, 8, 4, 32, -0.3),       # negative scale
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", SMALL_HEAD_CASES,
+                         ids=[f"{c[0]}-b{c[1]}-q{c[2]}-k{c[3]}-h{c[4]}-kv{c[5]}-d{c[6]}-s{c[7]}" for c in SMALL_HEAD_CASES])
+def test_small_heads_persistent(case, causal):
+    dt, b, s_q, s_k, h, h_kv, d, scale = case
+    say("attn_fwd small heads", case, "causal", causal)
+    q, k, v = workloads.make_qkv(b, s_q, s_k, h, d, dt, seed=23, h_kv=h_kv)
+    scale = 1 / math.sqrt(d) if scale is None else scale
+    O, L = run_fwd(q, k, v, scale, causal)
+    O_ref, L_ref = oracle.attention(*host64(q, k, v), scale, causal)
+    check(O, L, O_ref, L_ref, dt, str(case))
+
+
+@pytest.mark.parametrize("d", [16, 32])
+def test_small_heads_q_zero_closed_form(d):
+    # P = 1 on every visible key: LSE = ln(count) exactly and O = the mean of V
+    say("attn_fwd small heads Q=0", d)
+    _, k, v = workloads.make_qkv(40, 90, 150, 4, d, "fp16", seed=29)
+    q = torch.zeros((40, 90, 4, d), dtype=torch.float16)
+    for causal in (False, True):
+        O, L = run_fwd(q, k, v, 0.25, causal)
+        cnt = np.array([150 if not causal else i + 60 + 1 for i in range(90)], dtype=np.float64)
+        np.testing.assert_allclose(f64(L), np.broadcast_to(np.log(cnt), (40, 4, 90)), atol=1e-5)
+        vm = np.stack([f64(v)[:, :int(c)].mean(1) for c in cnt], 1)  # (b, s_q, h, d)
+        assert np.abs(f64(O) - vm).max() < TOL_O["fp16"]
+
+
 # ------------------------------------------------------------ edge cases ----
 
 @pytest.mark.parametrize("d", [16, 128])
