@@ -186,6 +186,11 @@ def cpu_baseline(w, budget_s: float = 12.0):
     }
 
 
+def progress(msg: str) -> None:
+    """One line on stderr as each part of the run ends (a long profiled run then shows progress)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def stats_ms(ts):
     """(median, min, mean) of a list of event times in ms."""
     ts = sorted(ts)
@@ -422,6 +427,7 @@ def main():
     if do_p:
         p_med, p_min, p_mean = stats_ms([e[0].elapsed_time(e[1]) for e in events])
         res["prefill"] = dict(ms=p_med, ms_min=p_min, ms_mean=p_mean, tflops=flops(wp) / (p_med * 1e-3) / 1e12)
+        progress(f"prefill timed: {p_med:.4f} ms median")
     if do_d:
         d_med, d_min, d_mean = stats_ms([e[2].elapsed_time(e[4]) for e in events])
         # Per-kernel durations of the two decode launches, from their own event
@@ -462,6 +468,7 @@ def main():
         res["decode"] = dict(ms=d_med, ms_min=d_min, ms_mean=d_mean, splitkv_ms=s_ms, combine_ms=c_ms,
                              gbs=kvb / (d_med * 1e-3) / 1e9, kv_bytes=kvb, splits=n_splits, sweep=sweep,
                              read=None if args.no_probes else read_ceiling(torch, probe, kvb, flush, dev, E))
+        progress(f"decode timed: {d_med * 1e3:.2f} us median")
 
     # ---- what the device sustains: shader clock during back-to-back prefill
     # launches, and the power-limited MFMA ceiling of a register-only loop
@@ -585,6 +592,7 @@ def main():
                     frac_hbm=round(kvb / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
             del q, k, v, kc, vc, table, sl, op, lp, O
         del flush_s
+        progress("smaller workloads timed")
 
     out = {
         "metric": "attn fwd TFLOP/s (prefill) & decode K/V GB/s, % of MI355X MFMA/HBM peak",
@@ -656,6 +664,7 @@ def main():
         out["other_workloads"] = side
     if args.only in ("all", "backward") and not args.no_small:
         out["backward"] = bench_backward(torch, ea, workloads, dev, E)
+        progress("backward timed")
         if args.only == "backward":
             bc5 = out["backward"]["C5"]
             out.update(value=bc5["tflops"], unit="TFLOP/s", config={
