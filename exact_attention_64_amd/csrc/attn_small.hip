@@ -38,6 +38,11 @@ __global__ __launch_bounds__(512) void small_kernel(const FwdParams p, int n_ite
   // NT key tiles (s_k > 32 (NT - 1)); one 32-row query block per wave
   const int nqb = blockDim.x / 64;
   const int slots = nqb + 2 * NT;  // 32-row tiles per item buffer: Q blocks, K tiles, V tiles
+  // fp16 at D = 16: NT tiles of ones after the two item buffers (see `vsrc`
+  // below).  (bf16 keeps 8 bits of P: its row sum is taken from P before the
+  // rounding, which keeps the log-sum-exp within 1e-3 when a few keys dominate.)
+  constexpr bool ONES_ROWS = D == 16 && T_ == kFP16;
+  char* const ones_lds = smem + 2 * slots * TB;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int off = p.s_k - p.s_q;
@@ -97,6 +102,11 @@ __global__ __launch_bounds__(512) void small_kernel(const FwdParams p, int n_ite
     const char* base = smem + buf * slots * TB;
     const char* kt0 = base + nqb * TB;
     const char* vt0 = base + (nqb + NT) * TB;
+    // At d = 16 rows 16..31 of the P V product's A operand (V^T) would repeat
+    // rows 0..15; with ONES_ROWS the half-waves that supply them read tiles of
+    // ones instead, so those accumulator rows come out as the row sum of the
+    // rounded P.
+    const char* vsrc = ONES_ROWS && (lane & 16) ? ones_lds : vt0;
     const int i = 32 * wave + l32;  // this lane's row
     u32x4_t qf[KK];
 #pragma unroll
@@ -155,9 +165,9 @@ __global__ __launch_bounds__(512) void small_kernel(const FwdParams p, int n_ite
 
     // P (0 where masked), its row sum, O^T += V^T P^T with P rounded to the
     // input type.  fp16: the row sum of the rounded P comes from the matrix core,
-    // a product with an A operand of ones (fp16 keeps 11 bits of P; bf16 sums P
-    // in fp32 on the vector ALU)
-    constexpr bool SUM_MFMA = T_ == kFP16;
+    // from the ones rows or else a product with an A operand of ones (fp16 keeps
+    // 11 bits of P; bf16 sums P in fp32 on the vector ALU)
+    constexpr bool SUM_MFMA = T_ == kFP16 && !ONES_ROWS;
     const u32x4_t ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
     f32x16_t acc[1], sum;
 #pragma unroll
@@ -179,25 +189,25 @@ __global__ __launch_bounds__(512) void small_kernel(const FwdParams p, int n_ite
             const int r = 8 * t16 + 2 * e + u;
             x[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sj[r], c, -mc));
             if (eg && !visible(j, r)) x[u] = 0.f;
-            if (!SUM_MFMA) l += x[u];
+            if (T_ != kFP16) l += x[u];
           }
           pb[t16][e] = Tt::pack2(x[0], x[1]);
         }
 #pragma unroll
       for (int t16 = 0; t16 < 2; ++t16) {
-        acc[0] = Tt::mfma(frag_cols<D>(vt0 + j * TB, lane, hi, 0, t16), pb[t16], acc[0]);
+        acc[0] = Tt::mfma(frag_cols<D>(vsrc + j * TB, lane, hi, 0, t16), pb[t16], acc[0]);
         if (SUM_MFMA) sum = Tt::mfma(ones, pb[t16], sum);
       }
       // the next tile's V^T reads stay after this tile's products (registers)
       __builtin_amdgcn_sched_barrier(0);
     }
-    l = SUM_MFMA ? sum[0] : pair_sum(l);
+    l = ONES_ROWS ? acc[0][8] : (SUM_MFMA ? sum[0] : pair_sum(l));
 
     if (i < p.s_q) {
       const bool any = l > 0.f;
       unsigned short* dst = (unsigned short*)p.o + (int64_t)bb * p.os[0] + (int64_t)i * p.os[1] +
                             (int64_t)hh * p.os[2];
-      store_cols<T_, D, 1>(dst, acc, hi, any ? 1.f / l : 0.f);
+      store_cols<T_, D, 1>(dst, acc, hi, any ? __builtin_amdgcn_rcpf(l) : 0.f);
       if (p.lse && hi == 0)
         p.lse[((int64_t)bb * p.h + hh) * p.s_q + i] = any ? (mc + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
     }
@@ -213,6 +223,10 @@ __global__ __launch_bounds__(512) void small_kernel(const FwdParams p, int n_ite
   const int step = (int)(gridDim.x / 8) + (xcd < (int)(gridDim.x % 8) ? 1 : 0);  // work-groups on this XCD
   int item = lo + m;
   if (item < hi_item) load_item(item, 0);
+  if constexpr (ONES_ROWS) {
+    for (int x = tid; x < NT * TB / 16; x += blockDim.x)
+      *(u32x4_t*)(ones_lds + 16 * x) = u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+  }
   // the first item lands here, on every path
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -246,7 +260,7 @@ template <int T_, int D, bool CAUSAL, int NT>
 hipError_t launch_small_nt(const FwdParams& p, hipStream_t st) {
   const int nqb = (p.s_q + 31) / 32;
   const int block = 64 * nqb;
-  const size_t lds = 2 * (size_t)(nqb + 2 * NT) * BTile<D>::BYTES;
+  const size_t lds = (2 * (size_t)(nqb + 2 * NT) + (D == 16 && T_ == kFP16 ? NT : 0)) * BTile<D>::BYTES;
   static std::mutex mu;
   static int cached[64][9] = {};
   int dev = 0;

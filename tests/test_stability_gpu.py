@@ -273,3 +273,52 @@ def test_constant_v_columns(case, causal):
         seen = np.isfinite(f64(L)).transpose(0, 2, 1)  # (b, s_q, h): rows that see a key
         assert np.all(np.abs(o[..., 3][seen] - 0.75) <= ULP[dt]), what
         assert np.all(np.abs(o[..., d - 1][seen] + 0.625) <= ULP[dt]), what
+
+
+SMALL_CASES = [
+    # dtype, b, s_q, s_k, h, h_kv, d: the persistent small-head kernel (d <= 32,
+    # both lengths <= 256).  Its single pass takes the reference from the first
+    # key tile, so every pattern here makes later keys score far above it.
+    ("fp16", 3, 150, 250, 4, 0, 16),
+    ("bf16", 3, 150, 250, 4, 0, 16),
+    ("fp16", 2, 100, 250, 4, 2, 32),
+    ("bf16", 2, 100, 250, 4, 2, 32),
+]
+SMALL_JUMPS = {77: 15.0, 140: 30.0, 230: 45.0}
+# a rise that keeps every P of the first pass finite and its row sums small
+SMALL_MILD = {100: 5.0, 200: 8.0}
+
+
+@pytest.mark.parametrize("pattern", ["planted", "ramp", "mild"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", SMALL_CASES, ids=[f"{c[0]}-b{c[1]}-q{c[2]}-k{c[3]}-h{c[4]}-kv{c[5]}-d{c[6]}" for c in SMALL_CASES])
+def test_rising_scores_small_heads(case, causal, pattern):
+    dt, b, s_q, s_k, h, h_kv, d = case
+    say("attn_fwd small heads", pattern, case, "causal", causal)
+    if pattern == "ramp":
+        q, k, v, scale = ramp(b, s_q, s_k, h, d, dt, seed=109, h_kv=h_kv)
+    else:
+        q, k, v, scale = planted(b, s_q, s_k, h, d, dt, seed=109, h_kv=h_kv,
+                                 jumps=SMALL_JUMPS if pattern == "planted" else SMALL_MILD)
+    O_ref, L_ref = oracle.attention(*host64(q, k, v), scale, causal)
+    assert np.nanmax(L_ref) > (6.0 if pattern == "mild" else 12.0)
+    O, L = ea.attn_fwd(*up(q, k, v), softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    check(O, L, O_ref, L_ref, dt, f"{case} {pattern}")
+
+
+@pytest.mark.parametrize("d", [16, 32])
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+def test_small_heads_scale8_and_key_shift(dt, d):
+    # Scores of +-8 sqrt(d) both ways, and K + 100 (every score of a row moved by
+    # scale * q.u), through the small-head kernel (s_k <= 256).
+    say("attn_fwd small heads scale 8 / key shift", dt, d)
+    q, k, v = workloads.make_qkv(2, 64, 200, 3, d, dt, seed=113)
+    ks = (k.float() + 100.0).to(k.dtype)
+    for kk, scale in ((k, 8.0), (ks, 1 / math.sqrt(d))):
+        for causal in (False, True):
+            O_ref, L_ref = oracle.attention(*host64(q, kk, v), scale, causal)
+            assert np.abs(L_ref).max() > 40
+            O, L = ea.attn_fwd(*up(q, kk, v), softmax_scale=scale, causal=causal)
+            torch.cuda.synchronize()
+            check(O, L, O_ref, L_ref, dt, f"scale {scale} causal={causal}", rel_lse=1e-5)
