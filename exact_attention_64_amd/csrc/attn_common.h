@@ -30,11 +30,15 @@ __device__ __forceinline__ To bitcast(const From& x) {
   return __builtin_bit_cast(To, x);
 }
 
-// Per-dtype pieces: the MFMA flavour and float -> storage rounding (nearest even).
+// Per-dtype pieces: the MFMA flavours (32x32x16 and 16x16x32) and float -> storage
+// rounding (nearest even).
 template <int DT> struct Ty;
 template <> struct Ty<kBF16> {
   static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ unsigned pack2(float x, float y) {
     bf16x2_t v = {(__bf16)x, (__bf16)y};
@@ -49,6 +53,9 @@ template <> struct Ty<kBF16> {
 template <> struct Ty<kFP16> {
   static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<f16x8_t>(a), bitcast<f16x8_t>(b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8_t>(a), bitcast<f16x8_t>(b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ unsigned pack2(float x, float y) {
     f16x2_t v = {(_Float16)x, (_Float16)y};

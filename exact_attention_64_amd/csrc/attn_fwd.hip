@@ -10,15 +10,19 @@
 // decoding second stage (reduce) code?").
 //
 // Data flow (one work-group = NW waves of 32 query rows each):
-//   Q fragment   : registers, loaded once, in the B-operand layout of
-//                  v_mfma_f32_32x32x16_{bf16,f16}.
+//   Q fragment   : registers, loaded once, in the B-operand layout of the
+//                  products: v_mfma_f32_16x16x32_{bf16,f16} at d >= 64 (two
+//                  16-row blocks per wave), v_mfma_f32_32x32x16 at d <= 32.
 //   K, V tiles   : 32 keys x D, global -> LDS with direct-to-LDS loads into a
 //                  ring of four slots per tensor, shared by the NW waves.
-//   S^T = K Q^T  : MFMA, so each lane owns one query row and 16 of every 32 keys
-//                  and the row maximum needs one permlane32 swap.
+//   S^T = K Q^T  : MFMA, so each lane owns query rows (two at d >= 64, 8 of
+//                  every 32 keys each; one at d <= 32, 16 keys) and a row
+//                  maximum is a reduction over 4 (or 2) lanes.
 //   P            : exp2 of the scaled scores minus the row's reference (log2(e)
 //                  folded into the scale), rounded to the input type.
 //   O^T += V^T P^T : MFMA; V^T fragments come from ds_read_b64_tr_b16.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace attn {
@@ -28,14 +32,17 @@ namespace attn {
 // 16-byte chunks.  Chunks are XOR-swizzled per row so that the two read
 // patterns below touch all 64 LDS banks without conflicts:
 //  K: ds_read_b128, 16 consecutive lanes read one chunk column of 16 rows;
-//  V: ds_read_b64_tr_b16, a half-wave reads 64 bytes of each of 4 rows.
+//  V: ds_read_b64_tr_b16, a half-wave reads 32 bytes (d >= 64) or 64 bytes
+//     (d <= 32) of each of 8 or 4 rows.
 template <int D> struct Swz {
   static constexpr int NCH = D / 8;
   static __device__ __forceinline__ int k(int row) {
     return (row / (16 / NCH)) % NCH;
   }
   static __device__ __forceinline__ int v(int row) {
-    return NCH == 16 ? 4 * (row % 4) : (NCH == 8 ? 4 * ((row / 2) % 2) : 0);
+    if constexpr (D == 128) return 2 * (row % 8);
+    else if constexpr (D == 64) return 2 * ((row / 2) % 4);
+    else return 0;
   }
 };
 
@@ -93,12 +100,24 @@ template <int T_, int D, int BN, int NW, int NBUF, bool PACK, bool NT, bool PAGE
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 64 ? 2 : 4, D >= 64 ? 2 : 4)))
 void fwdp_kernel(const FwdParams p) {
   using Tt = Ty<T_>;
-  constexpr int RB = 1, NB = 1;
-  static_assert(BN == 32, "one 32-key MFMA block per tile");
-  // CB: 32-row blocks of O^T; at d = 16 one block, whose upper 16 rows repeat
-  // the lower ones and are not stored.
-  constexpr int NCH = D / 8, KK = D / 16, CB = D >= 32 ? D / 32 : 1, BM = NW * 32;
-  constexpr int NT16 = BN / 16;
+  static_assert(BN == 32, "one 32-key tile per step");
+  // M16 (d >= 64): 16x16x32 products.  A wave's 32 query rows are RB = 2 blocks
+  // of 16 (lane l owns rows l % 16 and 16 + l % 16), a key tile NB = 2 blocks of
+  // 16 for S^T, KK products of 32 head columns each, O^T in CB = d / 16 blocks
+  // of 16 head columns, and one P operand of all 32 keys per row block.  Per
+  // flop these products move a fifth less accumulator and operand data through
+  // the registers than 32x32x16 ones, and under the package power limit the
+  // register-only softmax step ran 8% faster on them (2.15 against 1.92 GHz).
+  // Otherwise (d <= 32) 32x32x16 products, one 32-row block, 16 keys per lane;
+  // CB: 32-row blocks of O^T (at d = 16 one block, whose upper 16 rows repeat
+  // the lower ones and are not stored).
+  constexpr bool M16 = D >= 64;
+  constexpr int RB = M16 ? 2 : 1, NB = M16 ? 2 : 1;
+  constexpr int NCH = D / 8, KK = M16 ? D / 32 : D / 16, BM = NW * 32;
+  constexpr int CB = M16 ? D / 16 : (D >= 32 ? D / 32 : 1);
+  constexpr int NT16 = M16 ? 1 : BN / 16;
+  using Acc = typename std::conditional<M16, f32x4_t, f32x16_t>::type;
+  constexpr int NE = M16 ? 4 : 16;  // accumulator elements per lane
   constexpr int TILE = BN * D * 2;
   constexpr int NLOAD = TILE / 1024;            // 1 KB wave loads per tensor per tile
   constexpr int NLW = NLOAD < NW ? NLOAD : NW;  // waves that take part in the loads
@@ -128,6 +147,7 @@ void fwdp_kernel(const FwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const int l16 = lane & 15, g4 = lane >> 4;  // M16 lane position: column, 4-lane group
 
   const int nh = PACK ? p.h / p.g : p.h;  // heads indexed by the grid
   // Work items.  Causal: query tiles in order of decreasing work across all heads
@@ -157,13 +177,18 @@ void fwdp_kernel(const FwdParams p) {
   // keys of this batch entry: its own count when paged, else s_k
   const int s_k = PAGED ? min(max(p.seqlens_k[bb], 0), p.s_k) : p.s_k;
   const int off = s_k - p.s_q;
-  // This lane's row: query head my_h, position my_i (both uniform per
+  // This lane's rows: query head my_h, position my_i (both uniform per
   // work-group unless packed).  Position bounds for the masking decisions are
   // exact for one head's contiguous rows and conservative when packed.
-  const int rw = q0 + wave * 32 + l32;
-  const bool row_ok = rw < (PACK ? p.g * p.s_q : p.s_q);
-  const int my_i = PACK ? rw % p.s_q : rw;
-  const int my_h = PACK ? hk * p.g + rw / p.s_q : hg;
+  int my_i[RB], my_h[RB];
+  bool row_ok[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rw = q0 + wave * 32 + (M16 ? 16 * rb + l16 : l32);
+    row_ok[rb] = rw < (PACK ? p.g * p.s_q : p.s_q);
+    my_i[rb] = PACK ? rw % p.s_q : rw;
+    my_h[rb] = PACK ? hk * p.g + rw / p.s_q : hg;
+  }
   const int pos_wg_lo = PACK ? 0 : q0;
   const int pos_wg_hi = PACK ? p.s_q - 1 : q0 + BM - 1;
   const int pos_wave_lo = PACK ? 0 : q0 + wave * 32;
@@ -186,14 +211,15 @@ void fwdp_kernel(const FwdParams p) {
   const int* __restrict__ tbl = PAGED ? p.block_table + (int64_t)bb * p.bt_stride : nullptr;
   const int64_t ksr = p.ks[1], vsr = p.vs[1];
 
-  // Q fragments (B operand of S^T = K Q^T): this lane's row, d = hi*8 + 16*kk.
-  // Rows past the end are zero; a negative scale is folded in by negating Q, a
-  // zero scale by zeroing it.
+  // Q fragments (B operand of S^T = K Q^T): this lane's row of block rb, d =
+  // 32 kk + 8 g4 (M16) or 16 kk + 8 hi.  Rows past the end are zero; a negative
+  // scale is folded in by negating Q, a zero scale by zeroing it.
   u32x4_t qf[RB][KK];
-  auto fix_q = [&](u32x4_t x) {
-    if (!row_ok || p.zero_q) return u32x4_t{0u, 0u, 0u, 0u};
+  auto fix_q = [&](u32x4_t x, int rb) {
+    if (!row_ok[rb] || p.zero_q) return u32x4_t{0u, 0u, 0u, 0u};
     return p.neg_q ? (x ^ 0x80008000u) : x;
   };
+  auto q_chunk = [&](int kk) { return M16 ? 4 * kk + g4 : hi + 2 * kk; };  // 16-byte chunk of d
   if constexpr (QLDS) {
     // This wave's 32 rows into qbuf[wave], chunks swizzled as in a K tile; rows
     // past the end re-read the last row (zeroed once in registers).
@@ -210,27 +236,33 @@ void fwdp_kernel(const FwdParams p) {
       lds_dma16<false>((const void*)src, qbuf[wave] + i * 1024);
     }
   } else {
-    const unsigned short* __restrict__ Qr =
-        (const unsigned short*)p.q + (int64_t)bb * p.qs[0] + (int64_t)my_i * p.qs[1] + (int64_t)my_h * p.qs[2];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (row_ok && !p.zero_q) x = *(const u32x4_t*)(Qr + hi * 8 + kk * 16);
-      qf[0][kk] = fix_q(x);
+    for (int rb = 0; rb < RB; ++rb) {
+      const unsigned short* __restrict__ Qr = (const unsigned short*)p.q + (int64_t)bb * p.qs[0] +
+                                              (int64_t)my_i[rb] * p.qs[1] + (int64_t)my_h[rb] * p.qs[2];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        u32x4_t x = {0u, 0u, 0u, 0u};
+        if (row_ok[rb] && !p.zero_q) x = *(const u32x4_t*)(Qr + 8 * q_chunk(kk));
+        qf[rb][kk] = fix_q(x, rb);
+      }
     }
     // Wait for Q here, on every path: a load still pending where the key loop
     // starts would make the compiler wait for all loads (vmcnt(0)) inside it.
     __builtin_amdgcn_s_waitcnt(0);
   }
 
-  f32x16_t o[CB][RB];
+  Acc o[CB][RB];
   float m[RB], l[RB];
-  m[0] = -INFINITY;
-  l[0] = 0.f;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[cb][0][r] = 0.f;
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < NE; ++r) o[cb][rb][r] = 0.f;
+  }
   const float c = p.scale_log2;
 
   // ---- global -> LDS staging, 16 bytes per lane, by the first NLW waves.
@@ -295,29 +327,36 @@ void fwdp_kernel(const FwdParams p) {
   };
 
   // LDS -> registers: K fragments (A operand of S^T = K Q^T) of one tile, and
-  // V^T fragments (A operand of O^T += V^T P^T): d row cb*32 + l32, keys
-  // 16*t16 + 4*hi + {0..3} and 16*t16 + 8 + 4*hi + {0..3}, each half from one
-  // transposed read in which lane x of a 16-lane group fetches 4 columns of key
-  // row x / 4.
+  // V^T fragments (A operand of O^T += V^T P^T).
+  // M16: K block kb, product kk: key row 16 kb + l16, d chunk 4 kk + g4.  V^T
+  // block cb: head column 16 cb + l16 and the 8 keys of K slots 8 g4 .. 8 g4 + 7
+  // of the P V product, keys 4 g4 + {0..3} and 16 + 4 g4 + {0..3} (the keys the
+  // lane's S^T elements hold, so the P operand is the exponentiated S^T packed
+  // in place); each half from one transposed read in which lane x of a 16-lane
+  // group fetches 4 columns of key row x / 4 and receives column x of the 4 rows.
+  // Otherwise: K row l32, d chunk hi + 2 kk; V^T head column cb*32 + l32, keys
+  // 16*t16 + 4*hi + {0..3} and 16*t16 + 8 + 4*hi + {0..3}.
   const int g16 = (lane >> 4) & 1, xr = (lane & 15) >> 2, xq = lane & 3;
   auto read_k = [&](const char* kb, u32x4_t (&kf)[KK][NB]) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int row = l32;
-      const int ch = hi + 2 * kk;
-      kf[kk][0] = *(const u32x4_t*)(kb + row * D * 2 + 16 * (ch ^ Swz<D>::k(row)));
-    }
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int row = M16 ? 16 * b + l16 : l32;
+        const int ch = M16 ? 4 * kk + g4 : hi + 2 * kk;
+        kf[kk][b] = *(const u32x4_t*)(kb + row * D * 2 + 16 * (ch ^ Swz<D>::k(row)));
+      }
   };
   auto read_v = [&](const char* vb, u32x4_t (&vf)[CB][NT16]) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const int col = (cb * 32 + g16 * 16 + xq * 4) & (D >= 32 ? 0x7fffffff : D - 1);
+      const int col = M16 ? 16 * cb + 4 * xq : (cb * 32 + g16 * 16 + xq * 4) & (D >= 32 ? 0x7fffffff : D - 1);
       const int ch = col / 8, half = (col % 8) / 4;
 #pragma unroll
       for (int t16 = 0; t16 < NT16; ++t16)
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd) {
-          const int row = 16 * t16 + 8 * rd + 4 * hi + xr;
+          const int row = M16 ? 16 * rd + 4 * g4 + xr : 16 * t16 + 8 * rd + 4 * hi + xr;
           const char* a = vb + row * D * 2 + 16 * (ch ^ Swz<D>::v(row)) + 8 * half;
           const u32x2_t yy = bitcast<u32x2_t>(__builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(a)));
           vf[cb][t16][2 * rd] = yy[0];
@@ -325,67 +364,113 @@ void fwdp_kernel(const FwdParams p) {
         }
     }
   };
-  auto qk = [&](const u32x4_t (&kf)[KK][NB], f32x16_t (&s)[NB][RB]) {
+  // (M16: the four S^T blocks' products interleaved, so that no product waits
+  // on the one just issued)
+  auto qk = [&](const u32x4_t (&kf)[KK][NB], Acc (&s)[NB][RB]) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[0][0][r] = 0.f;
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) s[0][0] = Tt::mfma(kf[kk][0], qf[0][kk], s[0][0]);
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < NE; ++r) s[b][rb][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          if constexpr (M16) s[b][rb] = Tt::mfma16(kf[kk][b], qf[rb][kk], s[b][rb]);
+          else s[b][rb] = Tt::mfma(kf[kk][b], qf[rb][kk], s[b][rb]);
+        }
   };
   auto pv = [&](const u32x4_t (&vf)[CB][NT16], const u32x4_t (&pf)[RB][NT16]) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int t16 = 0; t16 < NT16; ++t16) o[cb][0] = Tt::mfma(vf[cb][t16], pf[0][t16], o[cb][0]);
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int t16 = 0; t16 < NT16; ++t16) {
+          if constexpr (M16) o[cb][rb] = Tt::mfma16(vf[cb][t16], pf[rb][t16], o[cb][rb]);
+          else o[cb][rb] = Tt::mfma(vf[cb][t16], pf[rb][t16], o[cb][rb]);
+        }
+  };
+  // key of S^T element r of key block b
+  auto key_of = [&](int k0, int b, int r) {
+    return M16 ? k0 + 16 * b + 4 * g4 + r : k0 + (r / 4) * 8 + hi * 4 + (r % 4);
   };
 
   // -inf for keys past the range end and (causal) keys after a row's diagonal.
-  auto mask_tile = [&](f32x16_t (&s)[NB][RB], int k0) {
-    const int i = my_i;
+  auto mask_tile = [&](Acc (&s)[NB][RB], int k0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = k0 + (r / 4) * 8 + hi * 4 + (r % 4);
-      if (key >= k_hi || (CAUSAL && key > i + off)) s[0][0][r] = -INFINITY;
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < NE; ++r) {
+          const int key = key_of(k0, b, r);
+          if (key >= k_hi || (CAUSAL && key > my_i[rb] + off)) s[b][rb][r] = -INFINITY;
+        }
+  };
+
+  // P = exp2(S * c - m) rounded to the input type; ls: this lane's sums per row.
+  // M16: the P operand of row block rb holds the lane's 8 keys in K-slot order,
+  // key block 0's four then key block 1's.
+  auto expo = [&](const Acc (&s)[NB][RB], u32x4_t (&pf)[RB][NT16], float (&ls)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float m_use = m[rb] == -INFINITY ? 0.f : m[rb];
+      float lsum = 0.f;
+#pragma unroll
+      for (int t16 = 0; t16 < NT16; ++t16) {
+        u32x4_t x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sa = M16 ? s[e / 2][rb][2 * (e % 2)] : s[0][rb][8 * t16 + 2 * e];
+          const float sb = M16 ? s[e / 2][rb][2 * (e % 2) + 1] : s[0][rb][8 * t16 + 2 * e + 1];
+          const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(sa, c, -m_use));
+          const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(sb, c, -m_use));
+          x[e] = Tt::pack2(a, b);
+          lsum += a + b;
+        }
+        pf[rb][t16] = x;
+      }
+      ls[rb] = lsum;
     }
   };
 
-  // P = exp2(S * c - m) rounded to the input type; returns this lane's row sum.
-  auto expo = [&](const f32x16_t (&s)[NB][RB], u32x4_t (&pf)[RB][NT16], float (&ls)[RB]) {
-    const float m_use = m[0] == -INFINITY ? 0.f : m[0];
-    float lsum = 0.f;
-#pragma unroll
-    for (int t16 = 0; t16 < NT16; ++t16) {
-      u32x4_t x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r0 = 8 * t16 + 2 * e;
-        const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][0][r0], c, -m_use));
-        const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][0][r0 + 1], c, -m_use));
-        x[e] = Tt::pack2(a, b);
-        lsum += a + b;
-      }
-      pf[0][t16] = x;
-    }
-    ls[0] = lsum;
+  // the maximum over the lanes that hold one row (4 at M16, 2 otherwise)
+  auto row_max = [&](float x) {
+    if constexpr (M16) x = fmaxf(x, __shfl_xor(x, 16));
+    return pair_max(x);
+  };
+  auto row_sum = [&](float x) {
+    if constexpr (M16) x += __shfl_xor(x, 16);
+    return pair_sum(x);
   };
 
   // Rare step: move each row's reference to max(m, tile max), rescale O and l,
   // and recompute this tile's P against the new reference.
-  auto rebase = [&](const f32x16_t (&s)[NB][RB], u32x4_t (&pf)[RB][NT16], float (&ls)[RB]) {
-    float mx = -INFINITY;
+  auto rebase = [&](const Acc (&s)[NB][RB], u32x4_t (&pf)[RB][NT16], float (&ls)[RB]) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[0][0][r]);
-    const float m_new = fmaxf(m[0], pair_max(mx) * c);
-    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[0] - m_new);
-    m[0] = m_new;
-    l[0] *= alpha;
+    for (int rb = 0; rb < RB; ++rb) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[cb][0][r] *= alpha;
+        for (int r = 0; r < NE; ++r) mx = fmaxf(mx, s[b][rb][r]);
+      const float m_new = fmaxf(m[rb], row_max(mx) * c);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rb] - m_new);
+      m[rb] = m_new;
+      l[rb] *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < NE; ++r) o[cb][rb][r] *= alpha;
+    }
     expo(s, pf, ls);
   };
 
-  f32x16_t sA[NB][RB], sB[NB][RB];
+  Acc sA[NB][RB], sB[NB][RB];
   u32x4_t pA[RB][NT16], pB[RB][NT16];
 
   // Prologue: K_0 and K_1, then the (K_{j+2}, V_j) pairs j < NBUF - 2, so that
@@ -412,8 +497,12 @@ void fwdp_kernel(const FwdParams p) {
   if constexpr (QLDS) {
     const char* qb = qbuf[wave];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      qf[0][kk] = fix_q(*(const u32x4_t*)(qb + l32 * D * 2 + 16 * ((hi + 2 * kk) ^ Swz<D>::k(l32))));
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = M16 ? 16 * rb + l16 : l32;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        qf[rb][kk] = fix_q(*(const u32x4_t*)(qb + row * D * 2 + 16 * (q_chunk(kk) ^ Swz<D>::k(row))), rb);
+    }
   }
   if (T > 0 && live) {
     u32x4_t kf[KK][NB];
@@ -436,7 +525,7 @@ void fwdp_kernel(const FwdParams p) {
   // (the scheduler cannot interleave across them); 2: interior step, where
   // moreover both loads exist and lie inside the key range and tile t needs no
   // mask, so the whole step is straight-line code apart from the rare rebase.
-  auto iter = [&](auto HC, int t, bool first, f32x16_t (&s)[NB][RB], f32x16_t (&s_next)[NB][RB],
+  auto iter = [&](auto HC, int t, bool first, Acc (&s)[NB][RB], Acc (&s_next)[NB][RB],
                   u32x4_t (&p_prev)[RB][NT16], u32x4_t (&p_cur)[RB][NT16],
                   char* kb_w, const char* kb_r, char* vb_w, const char* vb_r) __attribute__((always_inline)) {
     constexpr int hc = decltype(HC)::value;
@@ -456,9 +545,12 @@ void fwdp_kernel(const FwdParams p) {
       expo(s, p_cur, ls);
       if (has_next) qk(kf, s_next);
       __builtin_amdgcn_sched_barrier(0);
-      const bool bad = m[0] == -INFINITY || !(ls[0] <= PMAX);
+      bool bad = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) bad = bad || m[rb] == -INFINITY || !(ls[rb] <= PMAX);
       if (__builtin_amdgcn_ballot_w64(bad) != 0) rebase(s, p_cur, ls);
-      l[0] += ls[0];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) l[rb] += ls[rb];
     }
     asm volatile("" ::: "memory");
     if (hc == 2 || t + P + 1 < T) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0((P - 1) * PAIR));
@@ -504,41 +596,45 @@ void fwdp_kernel(const FwdParams p) {
     else pv(vf, pA);
   }
 
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
-  {
-    const int i = my_i, hh = my_h;
-    const float lt = pair_sum(l[0]);
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.  Element r of O^T
+  // block cb is head column 16 cb + 4 g4 + r (M16) or cb*32 + (r/4)*8 + 4 hi +
+  // r%4.
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int i = my_i[rb], hh = my_h[rb];
+    const float lt = row_sum(l[rb]);
     const bool has = lt > 0.f;
     const float inv = has ? 1.f / lt : 0.f;
-    const float lse = has ? (m[0] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
-    if (row_ok) {
+    const float lse = has ? (m[rb] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    const bool lse_lane = M16 ? g4 == 0 : hi == 0;
+    if (row_ok[rb]) {
       if (SPLIT) {
         const int64_t rowi = (((int64_t)split * p.b + bb) * p.h + hh) * p.s_q + i;
         float* op = p.o_part + rowi * D;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int col = cb * 32 + r4 * 8 + hi * 4;
+          for (int r4 = 0; r4 < NE / 4; ++r4) {
+            const int col = M16 ? 16 * cb + 4 * g4 : cb * 32 + r4 * 8 + hi * 4;
             if (col >= D) continue;
-            f32x4_t x = {o[cb][0][4 * r4] * inv, o[cb][0][4 * r4 + 1] * inv,
-                         o[cb][0][4 * r4 + 2] * inv, o[cb][0][4 * r4 + 3] * inv};
+            f32x4_t x = {o[cb][rb][4 * r4] * inv, o[cb][rb][4 * r4 + 1] * inv,
+                         o[cb][rb][4 * r4 + 2] * inv, o[cb][rb][4 * r4 + 3] * inv};
             *(f32x4_t*)(op + col) = x;
           }
-        if (hi == 0) p.lse_part[rowi] = lse;
+        if (lse_lane) p.lse_part[rowi] = lse;
       } else {
         unsigned short* op = (unsigned short*)p.o + (int64_t)bb * p.os[0] + (int64_t)i * p.os[1] + (int64_t)hh * p.os[2];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int col = cb * 32 + r4 * 8 + hi * 4;
+          for (int r4 = 0; r4 < NE / 4; ++r4) {
+            const int col = M16 ? 16 * cb + 4 * g4 : cb * 32 + r4 * 8 + hi * 4;
             if (col >= D) continue;
-            u32x2_t x = {Tt::pack2(o[cb][0][4 * r4] * inv, o[cb][0][4 * r4 + 1] * inv),
-                         Tt::pack2(o[cb][0][4 * r4 + 2] * inv, o[cb][0][4 * r4 + 3] * inv)};
+            u32x2_t x = {Tt::pack2(o[cb][rb][4 * r4] * inv, o[cb][rb][4 * r4 + 1] * inv),
+                         Tt::pack2(o[cb][rb][4 * r4 + 2] * inv, o[cb][rb][4 * r4 + 3] * inv)};
             *(u32x2_t*)(op + col) = x;
           }
-        if (hi == 0 && p.lse) p.lse[((int64_t)bb * p.h + hh) * p.s_q + i] = lse;
+        if (lse_lane && p.lse) p.lse[((int64_t)bb * p.h + hh) * p.s_q + i] = lse;
       }
     }
   }
