@@ -39,10 +39,12 @@ __global__ __launch_bounds__(512) void small_kernel(const FwdParams p, int n_ite
   const int nqb = blockDim.x / 64;
   const int slots = nqb + 2 * NT;  // 32-row tiles per item buffer: Q blocks, K tiles, V tiles
   // fp16 at D = 16: NT tiles of ones after the two item buffers (see `vsrc`
-  // below).  (bf16 keeps 8 bits of P: its row sum is taken from P before the
-  // rounding, which keeps the log-sum-exp within 1e-3 when a few keys dominate.)
+  // below), 128 bytes further on than a tile boundary so that the half-waves
+  // reading ones and those reading V in one transposed read use different banks.
+  // (bf16 keeps 8 bits of P: its row sum is taken from P before the rounding,
+  // which keeps the log-sum-exp within 1e-3 when a few keys dominate.)
   constexpr bool ONES_ROWS = D == 16 && T_ == kFP16;
-  char* const ones_lds = smem + 2 * slots * TB;
+  char* const ones_lds = smem + 2 * slots * TB + 128;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int off = p.s_k - p.s_q;
@@ -260,7 +262,8 @@ template <int T_, int D, bool CAUSAL, int NT>
 hipError_t launch_small_nt(const FwdParams& p, hipStream_t st) {
   const int nqb = (p.s_q + 31) / 32;
   const int block = 64 * nqb;
-  const size_t lds = (2 * (size_t)(nqb + 2 * NT) + (D == 16 && T_ == kFP16 ? NT : 0)) * BTile<D>::BYTES;
+  const size_t lds = (2 * (size_t)(nqb + 2 * NT) + (D == 16 && T_ == kFP16 ? NT : 0)) * BTile<D>::BYTES +
+                     (D == 16 && T_ == kFP16 ? 128 : 0);
   static std::mutex mu;
   static int cached[64][9] = {};
   int dev = 0;
