@@ -111,9 +111,13 @@ void fwdp_kernel(const FwdParams p) {
   // Otherwise (d <= 32) 32x32x16 products, one 32-row block, 16 keys per lane;
   // CB: 32-row blocks of O^T (at d = 16 one block, whose upper 16 rows repeat
   // the lower ones and are not stored).
+  // Packed groups on 4 waves (at most 64 rows: a few query heads of a few
+  // positions) take one 16-row block per wave (WR = 16 rows), so that the rows
+  // spread over more waves and SIMDs instead of filling one wave.
   constexpr bool M16 = D >= 64;
-  constexpr int RB = M16 ? 2 : 1, NB = M16 ? 2 : 1;
-  constexpr int NCH = D / 8, KK = M16 ? D / 32 : D / 16, BM = NW * 32;
+  constexpr int RB = M16 ? (PACK && NW == 4 ? 1 : 2) : 1, NB = M16 ? 2 : 1;
+  constexpr int WR = M16 ? 16 * RB : 32;  // query rows per wave
+  constexpr int NCH = D / 8, KK = M16 ? D / 32 : D / 16, BM = NW * WR;
   constexpr int CB = M16 ? D / 16 : (D >= 32 ? D / 32 : 1);
   constexpr int NT16 = M16 ? 1 : BN / 16;
   using Acc = typename std::conditional<M16, f32x4_t, f32x16_t>::type;
@@ -138,6 +142,7 @@ void fwdp_kernel(const FwdParams p) {
   // on its own first).  Used where the extra NW * TILE bytes of LDS cost no
   // occupancy: the 8-wave launch (one work-group per compute unit) and d = 16.
   constexpr bool QLDS = NW == 8 || D == 16;
+  static_assert(!QLDS || WR == 32, "Q through LDS fills 32 rows per wave");
   __shared__ __attribute__((aligned(1024))) char kbuf[NBUF][TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf[NBUF][TILE];
   __shared__ __attribute__((aligned(1024))) char qbuf[QLDS ? NW : 1][QLDS ? TILE : 16];
@@ -184,19 +189,19 @@ void fwdp_kernel(const FwdParams p) {
   bool row_ok[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int rw = q0 + wave * 32 + (M16 ? 16 * rb + l16 : l32);
+    const int rw = q0 + wave * WR + (M16 ? 16 * rb + l16 : l32);
     row_ok[rb] = rw < (PACK ? p.g * p.s_q : p.s_q);
     my_i[rb] = PACK ? rw % p.s_q : rw;
     my_h[rb] = PACK ? hk * p.g + rw / p.s_q : hg;
   }
   const int pos_wg_lo = PACK ? 0 : q0;
   const int pos_wg_hi = PACK ? p.s_q - 1 : q0 + BM - 1;
-  const int pos_wave_lo = PACK ? 0 : q0 + wave * 32;
+  const int pos_wave_lo = PACK ? 0 : q0 + wave * WR;
   // A wave with no rows at all only loads its share of each tile: packed
   // work-groups often have such waves (6 heads x 1 row fill one wave of eight),
   // and so does the last query tile of a head whose length is not a multiple of
   // the work-group's rows (s_q = 150 over 128-row work-groups: three of four).
-  const bool live = q0 + wave * 32 < (PACK ? p.g * p.s_q : p.s_q);
+  const bool live = q0 + wave * WR < (PACK ? p.g * p.s_q : p.s_q);
 
   int k_lo = 0, k_hi = s_k;
   if (SPLIT) {
@@ -648,7 +653,7 @@ void fwdp_kernel(const FwdParams p) {
 // kPrefillNBUF.
 template <int T_, int D, int NW, bool PACK, bool NT, bool PAGED, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwdp_t(const FwdParams& p, hipStream_t st) {
-  constexpr int BM = NW * 32;
+  constexpr int BM = NW * (D >= 64 && PACK && NW == 4 ? 16 : 32);  // the kernel's rows per work-group
   constexpr int NBUF = D == 16 ? 8 : kPrefillNBUF;
   FwdParams q = p;
   const int64_t rows = PACK ? (int64_t)p.g * p.s_q : p.s_q;
@@ -661,7 +666,8 @@ static hipError_t launch_fwdp_t(const FwdParams& p, hipStream_t st) {
 }
 
 // Launch shape at d >= 64 from the rows one head (or packed group) brings:
-//  - at most 128 (decode and short chunks): 4 waves, so two work-groups share a
+//  - at most 128 (decode and short chunks; 64 for packed groups, whose 4-wave
+//    work-groups take 16 rows per wave): 4 waves, so two work-groups share a
 //    compute unit and twice as many key streams are in flight (measured 1.66x
 //    faster than 8 waves on b = 8, h = 48, s_q = 4, 4096 keys);
 //  - otherwise 8 waves (256 rows) sharing each K/V tile.
@@ -672,7 +678,7 @@ static hipError_t launch_fwdp_t(const FwdParams& p, hipStream_t st) {
 template <int T_, int D, bool PACK, bool PAGED, bool CAUSAL, bool SPLIT>
 static hipError_t launch_fwd_rows(const FwdParams& p, hipStream_t st) {
   const int64_t rows = PACK ? (int64_t)p.g * p.s_q : p.s_q;
-  if (rows <= 4 * 32) return launch_fwdp_t<T_, D, 4, PACK, true, PAGED, CAUSAL, SPLIT>(p, st);
+  if (rows <= 4 * (PACK ? 16 : 32)) return launch_fwdp_t<T_, D, 4, PACK, true, PAGED, CAUSAL, SPLIT>(p, st);
   if ((rows + kPrefillNW * 32 - 1) / (kPrefillNW * 32) <= kStreamQTiles)
     return launch_fwdp_t<T_, D, kPrefillNW, PACK, true, PAGED, CAUSAL, SPLIT>(p, st);
   return launch_fwdp_t<T_, D, kPrefillNW, PACK, false, PAGED, CAUSAL, SPLIT>(p, st);
