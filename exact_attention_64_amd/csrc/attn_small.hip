@@ -19,7 +19,9 @@
 // P = exp2((s - max) * scale * log2 e), the row sum and O^T += V^T P^T.  The
 // second pass forms S^T again instead of keeping it in registers: the matrix
 // core has time to spare at these head dims, and the registers saved keep more
-// waves resident.  O = O / sum, LSE = max + ln(sum).
+// waves resident.  O = O / sum, LSE = max + ln(sum).  (fp16 at d = 16 takes one
+// pass against tile 0's maximum first and the two passes only where a row sum
+// shows a later score far above it.)
 #include <mutex>
 
 #include "attn_common.h"
@@ -147,63 +149,135 @@ __global__ __launch_bounds__(512) void small_kernel(const FwdParams p, int n_ite
       const int key = 32 * j + (r / 4) * 8 + 4 * hi + (r % 4);
       return key < p.s_k && (!CAUSAL || key <= i + off);
     };
-    // the row maximum over visible keys (the two half-waves hold the two halves
-    // of each tile's keys for the same rows)
-    float m = -INFINITY;
+    float m, mc, l;
+    f32x16_t acc[1];
+    if constexpr (ONES_ROWS) {
+      // fp16 at d = 16: one pass against a reference from tile 0 (any reference
+      // gives the same quotient, section 3.3: a common factor of O and the sum
+      // cancels), the two-pass form as fallback.  A row that sees any key sees key
+      // 0 (causal visibility is a prefix), so a row whose reference is -inf sees
+      // nothing.  Against tile 0's maximum every P of a row is at most its sum l
+      // (the largest at least 1): l <= 2^20 keeps every rounded P finite.
+      // Otherwise (or l NaN) the wave takes the row maximum over all tiles,
+      // against which every P is at most 1, and repeats the pass.
+      auto tile_max = [&](int j, const f32x16_t& sj, float mm) __attribute__((always_inline)) {
+        if (edge(j)) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      if (!live(j)) continue;
-      const f32x16_t sj = scores(j);
-      if (edge(j)) {
+          for (int r = 0; r < 16; ++r) mm = fmaxf(mm, visible(j, r) ? sj[r] : -INFINITY);
+        } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) m = fmaxf(m, visible(j, r) ? sj[r] : -INFINITY);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) m = fmaxf(m, sj[r]);
-      }
-    }
-    m = pair_max(m);
-    const float mc = m == -INFINITY ? 0.f : m * c;
-
-    // P (0 where masked), its row sum, O^T += V^T P^T with P rounded to the
-    // input type.  fp16: the row sum of the rounded P comes from the matrix core,
-    // from the ones rows or else a product with an A operand of ones (fp16 keeps
-    // 11 bits of P; bf16 sums P in fp32 on the vector ALU)
-    constexpr bool SUM_MFMA = T_ == kFP16 && !ONES_ROWS;
-    const u32x4_t ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
-    f32x16_t acc[1], sum;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[0][r] = sum[r] = 0.f;
-    float l = 0.f;
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      if (!live(j)) continue;
-      const bool eg = edge(j);
-      const f32x16_t sj = scores(j);
-      u32x4_t pb[2];
-#pragma unroll
-      for (int t16 = 0; t16 < 2; ++t16)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r = 8 * t16 + 2 * e + u;
-            x[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sj[r], c, -mc));
-            if (eg && !visible(j, r)) x[u] = 0.f;
-            if (T_ != kFP16) l += x[u];
-          }
-          pb[t16][e] = Tt::pack2(x[0], x[1]);
+          for (int r = 0; r < 16; ++r) mm = fmaxf(mm, sj[r]);
         }
+        return mm;
+      };
+      // P = exp2(s c - mc), 0 where masked, rounded to fp16, O^T += V^T P^T; the
+      // row sum of the rounded P comes from the ones rows.  S0: tile 0's scores
+      // are already formed, in s0.
+      auto pass = [&](auto S0, float mc_, const f32x16_t& s0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int t16 = 0; t16 < 2; ++t16) {
-        acc[0] = Tt::mfma(frag_cols<D>(vsrc + j * TB, lane, hi, 0, t16), pb[t16], acc[0]);
-        if (SUM_MFMA) sum = Tt::mfma(ones, pb[t16], sum);
+        for (int r = 0; r < 16; ++r) acc[0][r] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          if (!live(j)) continue;
+          const bool eg = edge(j);
+          const f32x16_t sj = decltype(S0)::value && j == 0 ? s0 : scores(j);
+          u32x4_t pb[2];
+#pragma unroll
+          for (int t16 = 0; t16 < 2; ++t16)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float x[2];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const int r = 8 * t16 + 2 * e + u;
+                x[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sj[r], c, -mc_));
+                if (eg && !visible(j, r)) x[u] = 0.f;
+              }
+              pb[t16][e] = Tt::pack2(x[0], x[1]);
+            }
+#pragma unroll
+          for (int t16 = 0; t16 < 2; ++t16)
+            acc[0] = Tt::mfma(frag_cols<D>(vsrc + j * TB, lane, hi, 0, t16), pb[t16], acc[0]);
+          // the next tile's V^T reads stay after this tile's products (registers)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        return acc[0][8];
+      };
+      f32x16_t s0;
+      m = -INFINITY;
+      if (live(0)) {
+        s0 = scores(0);
+        m = pair_max(tile_max(0, s0, m));
       }
-      // the next tile's V^T reads stay after this tile's products (registers)
-      __builtin_amdgcn_sched_barrier(0);
+      mc = m == -INFINITY ? 0.f : m * c;
+      l = pass(IC<1>{}, mc, s0);
+      if (__builtin_amdgcn_ballot_w64(!(l <= 0x1p20f)) != 0) {
+#pragma unroll
+        for (int j = 1; j < NT; ++j)
+          if (live(j)) m = tile_max(j, scores(j), m);
+        m = pair_max(m);
+        mc = m == -INFINITY ? 0.f : m * c;
+        l = pass(IC<0>{}, mc, s0);
+      }
+    } else {
+      // the row maximum over visible keys (the two half-waves hold the two halves
+      // of each tile's keys for the same rows)
+      m = -INFINITY;
+  #pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        if (!live(j)) continue;
+        const f32x16_t sj = scores(j);
+        if (edge(j)) {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) m = fmaxf(m, visible(j, r) ? sj[r] : -INFINITY);
+        } else {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) m = fmaxf(m, sj[r]);
+        }
+      }
+      m = pair_max(m);
+      mc = m == -INFINITY ? 0.f : m * c;
+
+      // P (0 where masked), its row sum, O^T += V^T P^T with P rounded to the
+      // input type.  fp16: the row sum of the rounded P comes from the matrix core,
+      // from the ones rows or else a product with an A operand of ones (fp16 keeps
+      // 11 bits of P; bf16 sums P in fp32 on the vector ALU)
+      constexpr bool SUM_MFMA = T_ == kFP16 && !ONES_ROWS;
+      const u32x4_t ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+      f32x16_t sum;
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) acc[0][r] = sum[r] = 0.f;
+      l = 0.f;
+  #pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        if (!live(j)) continue;
+        const bool eg = edge(j);
+        const f32x16_t sj = scores(j);
+        u32x4_t pb[2];
+  #pragma unroll
+        for (int t16 = 0; t16 < 2; ++t16)
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x[2];
+  #pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int r = 8 * t16 + 2 * e + u;
+              x[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sj[r], c, -mc));
+              if (eg && !visible(j, r)) x[u] = 0.f;
+              if (T_ != kFP16) l += x[u];
+            }
+            pb[t16][e] = Tt::pack2(x[0], x[1]);
+          }
+  #pragma unroll
+        for (int t16 = 0; t16 < 2; ++t16) {
+          acc[0] = Tt::mfma(frag_cols<D>(vsrc + j * TB, lane, hi, 0, t16), pb[t16], acc[0]);
+          if (SUM_MFMA) sum = Tt::mfma(ones, pb[t16], sum);
+        }
+        // the next tile's V^T reads stay after this tile's products (registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l = ONES_ROWS ? acc[0][8] : (SUM_MFMA ? sum[0] : pair_sum(l));
     }
-    l = ONES_ROWS ? acc[0][8] : (SUM_MFMA ? sum[0] : pair_sum(l));
 
     if (i < p.s_q) {
       const bool any = l > 0.f;
