@@ -246,6 +246,9 @@ PACKED_CASES = [
     ("fp16", 2, 1, 2049, 32, 4, 64, False, 7),     # one row per head, 8 heads per K/V head
     ("bf16", 1, 5, 333, 12, 3, 128, True, 1),
     ("fp16", 2, 9, 64, 6, 2, 128, True, 64),       # one key per split
+    ("bf16", 2, 16, 900, 12, 2, 128, True, 3),     # 96 packed rows: the 8-wave launch
+    ("fp16", 1, 9, 500, 16, 2, 64, False, 2),      # 72 packed rows at d = 64
+    ("bf16", 2, 16, 400, 16, 4, 128, False, 2),    # 64 packed rows: four waves of 16 rows, all full
 ]
 
 
@@ -298,6 +301,7 @@ PAGED_CASES = [
     ("fp16", 3, 2, 6, 6, 64, [95, 1, 64], 32, True, 2),
     ("bf16", 3, 1, 5, 5, 64, [1000, 0, 33], 32, True, 7),       # one-row decode kernel: 64-key batches
     ("bf16", 2, 1, 3, 3, 128, [4097, 31], 64, False, 3),        # over three 32-key blocks; mixed lengths
+    ("bf16", 2, 12, 12, 2, 128, [700, 300], 64, True, 2),       # 72 packed rows per K/V head: 8 waves
 ]
 
 
