@@ -546,6 +546,11 @@ void fwdp_kernel(const FwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
       float ls[RB];
       if (!first) pv(vf, p_prev);
+      // M16: the P V products issue as one group, ahead of the K reads,
+      // exponentials and score products that the scheduler interleaves (left
+      // free to mix all of them it took 4-5% more cycles on the 16k causal
+      // prefill)
+      if constexpr (M16) __builtin_amdgcn_sched_barrier(0);
       if (has_next) read_k(kb_r, kf);
       expo(s, p_cur, ls);
       if (has_next) qk(kf, s_next);
